@@ -1,0 +1,30 @@
+"""Compile the CPU oracle into oracle/liboracle.so (gcc, no fast-math).
+
+Test infrastructure: only the tests, the smoke check and the benchmark's
+CPU-baseline leg use the library this builds.
+"""
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+# -ffp-contract=off: every float operation in the oracle is rounded on its
+# own; -fno-fast-math is gcc's default and is spelled out for the reader.
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
+          "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(LIB + ".tmp", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
