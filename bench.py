@@ -1,0 +1,294 @@
+#!/usr/bin/env python3
+"""Benchmark of the Ulysses 4D relayout on one MI355X.
+
+One step = one mode-0 relayout plus one mode-1 relayout of the video-DiT
+attention operand the fast-ulysses pages measure on (Wan 720p, bf16):
+W = 8 emulated ranks, 75,600 tokens (9,450 per rank), 40 heads (5 per rank),
+head dim 128, batch 1.  Synthetic N(0, 1) inputs, resident in HBM before
+the timed region.  Mode 1 reads a separately generated head-sharded input,
+so no step reads what the previous kernel just wrote (no help from the
+256 MB Infinity Cache).
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value      whole-step throughput, algorithmic bytes (every element read
+             once and written once) / step time, in GB/s;
+  roofline   the relayout kernel: algorithmic bytes per launch / its
+             average launch time from HIP events on the launch stream,
+             against 8 TB/s; `traffic` comes from the rocprofv3 counter
+             summary in profiles/ when it was taken on the current kernel
+             source, else null;
+  cpu_baseline  the CPU oracle (single thread) on a bounded sample;
+  rows       the other hot-path rows timed after the step: uneven W=7 in
+             four dtypes, the plane-at-a-time QKV pack, the fused QK-norm +
+             RoPE scatter; plus a same-run device-to-device copy ceiling.
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PEAK_GBS = 8000.0   # MI355X HBM3E, AMD's published peak
+METRIC = "relayout HBM GB/s & % of MI355X peak, W=8 75.6k-token bf16 mode0+mode1"
+COUNTERS = os.path.join(ROOT, "profiles", "relayout_w8_wan720p_counters.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "args.hpp"):
+        with open(os.path.join(ROOT, "sequence_attention_relayout_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            c = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def timed(fn, reps, stream, torch):
+    """Median and min milliseconds of fn() over reps, HIP events on `stream`."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) for a, b in evs]
+    return statistics.median(ts), min(ts)
+
+
+def cpu_baseline():
+    """The oracle as it is, one thread, on half the tokens of the workload."""
+    import numpy as np
+    import oracle
+    world, per_rank, heads, d = 8, 4725, 5, 128
+    seq, head = [per_rank] * world, [heads] * world
+    rng = np.random.default_rng(7)
+    xs = [rng.integers(0, 1 << 16, (1, per_rank, heads * world, d), dtype=np.uint16)
+          for _ in range(world)]
+    ys_in = [rng.integers(0, 1 << 16, (1, per_rank * world, heads, d), dtype=np.uint16)
+             for _ in range(world)]
+    t0 = time.perf_counter()
+    oracle.a2a_4d(0, 1, d, seq, head, xs)
+    oracle.a2a_4d(1, 1, d, seq, head, ys_in)
+    dt = time.perf_counter() - t0
+    nbytes = 2 * 2 * (per_rank * world) * (heads * world) * d * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"W=8, {per_rank * world} tokens ({per_rank} per rank, half of the "
+                      "workload), n=40, d=128, bf16: one mode 0 and one mode 1 on the oracle's "
+                      f"plain index loops, single thread, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="time the step only")
+    args = ap.parse_args()
+    world_env = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world_env != 1:
+        print("bench.py measures one GPU: the W ranks are emulated as shard buffers in one "
+              "GPU's HBM, and this build has no multi-GPU path. Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    sys.path.insert(0, ROOT)
+    from sequence_attention_relayout_amd import ulysses as U
+    from sequence_attention_relayout_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+    U.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs, {props.total_memory / 2**30:.0f} GiB")
+
+    wl = W.workloads()["w8_wan720p"]
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
+    bytes0, bytes1 = U.ulysses_plan_bytes(plan, 0), U.ulysses_plan_bytes(plan, 1)
+    step_bytes = bytes0 + bytes1
+    x0 = W.make_shards(wl, 0, "bf16", wl.seed, dev)
+    y0 = [torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16, device=dev)
+          for r in range(wl.world)]
+    y1 = W.make_shards(wl, 1, "bf16", wl.seed + 1, dev)
+    x1 = [torch.empty(U.ulysses_plan_shape(plan, 1, r, True), dtype=torch.bfloat16, device=dev)
+          for r in range(wl.world)]
+    torch.cuda.synchronize()
+    h = stream.cuda_stream
+
+    def mode0():
+        U.ulysses_a2a_4d(plan, 0, x0, y0, h)
+
+    def mode1():
+        U.ulysses_a2a_4d(plan, 1, y1, x1, h)
+
+    for _ in range(args.warmup):
+        mode0()
+        mode1()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for k in range(K):
+        evs[k][0].record(stream)
+        mode0()
+        evs[k][1].record(stream)
+        mode1()
+        evs[k][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    m0 = [e[0].elapsed_time(e[1]) for e in evs]
+    m1 = [e[1].elapsed_time(e[2]) for e in evs]
+    launch_ms = statistics.mean(m0 + m1)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    achieved = (step_bytes / 2) / (launch_ms * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); mode 0 median "
+        f"{statistics.median(m0) * 1e3:.1f} us, mode 1 median {statistics.median(m1) * 1e3:.1f} us;"
+        f" host wall {wall / K * 1e3:.1f} us/step")
+
+    # same-run device-to-device copy of one shard set's bytes: the flat-copy
+    # ceiling ("of the fabric" in the pages' terms)
+    flat_src = torch.empty(bytes0 // 2, dtype=torch.uint8, device=dev)
+    flat_dst = torch.empty_like(flat_src)
+    d2d_ms, _ = timed(lambda: flat_dst.copy_(flat_src), 10, stream, torch)
+    d2d = bytes0 / (d2d_ms * 1e-3) / 1e9
+    del flat_src, flat_dst
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "w8_wan720p: mode 0 + mode 1, W=8 emulated ranks, b=1, "
+                               "s_global=75,600 (9,450/rank), n_global=40 (5/rank), d=128",
+                   "world": 8, "b": 1, "s_global": 75600, "n_global": 40, "d": 128,
+                   "bytes_per_step": step_bytes, "parallelism": "none (one GPU)"},
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "relayout_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic_from_profile(),
+                     "bytes_per_launch": bytes0, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     "launches_timed": 2 * K},
+        "d2d_copy_ceiling_gbs": round(d2d, 1),
+    }
+    del x0, y0, y1, x1
+    torch.cuda.empty_cache()
+
+    if not args.no_rows:
+        result["rows"] = time_rows(U, W, torch, dev, stream)
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle on a bounded sample ...")
+        result["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(result), flush=True)
+
+
+def time_rows(U, W, torch, dev, stream, reps=10):
+    """The other hot-path rows, each timed on its own (median of reps)."""
+    rows = {}
+    h = stream.cuda_stream
+    wls = W.workloads()
+
+    wl = wls["w7_uneven"]
+    for dt in wl.dtypes:
+        plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, dt)
+        for mode in (0, 1):
+            xs = W.make_shards(wl, mode, dt, 40 + mode, dev)
+            ys = [torch.empty(U.ulysses_plan_shape(plan, mode, r, True),
+                              dtype=W.torch_dtype(dt), device=dev) for r in range(wl.world)]
+            med, mn = timed(lambda: U.ulysses_a2a_4d(plan, mode, xs, ys, h), reps, stream, torch)
+            nb = U.ulysses_plan_bytes(plan, mode)
+            rows[f"w7_uneven_{dt}_mode{mode}"] = {
+                "gbs": round(nb / (med * 1e-3) / 1e9, 1), "median_us": round(med * 1e3, 1),
+                "bytes": nb}
+            del xs, ys
+        torch.cuda.empty_cache()
+    log("uneven rows done")
+
+    wl = wls["w4_qkv_chunked"]
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16",
+                                 wl.window_cap_bytes)
+    xs = W.make_shards(wl, 0, "bf16", wl.seed, dev)
+    ys = [torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16, device=dev)
+          for r in range(wl.world)]
+    win = [torch.empty(U.ulysses_plan_window_bytes(plan, 0), dtype=torch.uint8, device=dev)
+           for _ in range(wl.world)]
+    med, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win, h), 3, stream, torch)
+    relayout_bytes = U.ulysses_plan_bytes(plan, 0)
+    rows["w4_qkv_chunked_mode0"] = {
+        "gbs_relayout_bytes": round(relayout_bytes / (med * 1e-3) / 1e9, 1),
+        "gbs_moved_bytes": round(2 * relayout_bytes / (med * 1e-3) / 1e9, 1),
+        "median_us": round(med * 1e3, 1), "relayout_bytes": relayout_bytes,
+        "moved_bytes_incl_window_copy": 2 * relayout_bytes}
+    med, _ = timed(lambda: U.ulysses_a2a_4d(plan, 0, xs, ys, h), 3, stream, torch)
+    rows["w4_qkv_direct_mode0"] = {"gbs": round(relayout_bytes / (med * 1e-3) / 1e9, 1),
+                                   "median_us": round(med * 1e3, 1)}
+    del xs, ys, win
+    torch.cuda.empty_cache()
+    log("chunked rows done")
+
+    wl = wls["w8_fused_qknorm_rope"]
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
+    q = W.make_shards(wl, 0, "bf16", 70, dev)
+    k = W.make_shards(wl, 0, "bf16", 71, dev)
+    v = W.make_shards(wl, 0, "bf16", 72, dev)
+    outs = [[torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16,
+                         device=dev) for r in range(wl.world)] for _ in range(3)]
+    gq, gk = W.make_gamma(wl.d, 73, dev), W.make_gamma(wl.d, 74, dev)
+    c, s = U.ulysses_rope_table(10000.0, wl.s_global, wl.d)
+    tc, ts = torch.from_numpy(c).to(dev), torch.from_numpy(s).to(dev)
+
+    def fused():
+        U.ulysses_a2a_4d_qknorm_rope(plan, q, outs[0], k, outs[1], gq, gk, 1e-6, tc, ts, h)
+
+    def plain_v():
+        U.ulysses_a2a_4d(plan, 0, v, outs[2], h)
+
+    fmed, _ = timed(fused, reps, stream, torch)
+    vmed, _ = timed(plain_v, reps, stream, torch)
+    qk_bytes = 2 * U.ulysses_plan_bytes(plan, 0) + c.nbytes + s.nbytes + 2 * wl.d * 4
+    v_bytes = U.ulysses_plan_bytes(plan, 0)
+    rows["w8_fused_qknorm_rope"] = {
+        "fused_qk_gbs": round(qk_bytes / (fmed * 1e-3) / 1e9, 1),
+        "fused_qk_median_us": round(fmed * 1e3, 1),
+        "plain_v_gbs": round(v_bytes / (vmed * 1e-3) / 1e9, 1),
+        "total_gbs": round((qk_bytes + v_bytes) / ((fmed + vmed) * 1e-3) / 1e9, 1),
+        "bytes": qk_bytes + v_bytes}
+    del q, k, v, outs
+    torch.cuda.empty_cache()
+    log("fused rows done")
+    return rows
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,68 @@
+"""Build libulysses.so in-tree for gfx950.
+
+kernels.hip goes through hipcc (device code for gfx950 only); the plan and
+the C ABI are plain host C++ built with g++ against the HIP runtime headers.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libulysses.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra",
+              "-D__HIP_PLATFORM_AMD__", f"-I{ROCM}/include"]
+# -ffp-contract=off: the fused path rounds every product on its own.
+# -packed-fp32-ops off: no packed fp32 instructions in any kernel.
+DEVICE_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+                "-ffp-contract=off", "-Xclang", "-target-feature", "-Xclang",
+                "-packed-fp32-ops", "-Wall"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
+    """Compile and link; `defines` (e.g. ["ULY_UNROLL=8"]) override the
+    kernels' compile-time launch constants."""
+    os.makedirs(build_dir, exist_ok=True)
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    dflags = [f"-D{d}" for d in defines]
+    objs = []
+    for src in ("plan.cpp", "capi.cpp"):
+        obj = os.path.join(build_dir, src.replace(".cpp", ".o"))
+        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    kobj = os.path.join(build_dir, "kernels.o")
+    _run([hipcc, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj],
+         verbose)
+    objs.append(kobj)
+    tmp = out + ".tmp"
+    _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
+
+
+def build_plan_test(verbose=False, build_dir=BUILD):
+    """Host-only test driver of the plan (no HIP): tests/native/plan_test.cpp."""
+    os.makedirs(build_dir, exist_ok=True)
+    exe = os.path.join(build_dir, "plan_test")
+    _run(["g++", "-O2", "-std=c++17", "-Wall", f"-I{CSRC}",
+          os.path.join(ROOT, "tests", "native", "plan_test.cpp"),
+          os.path.join(CSRC, "plan.cpp"), "-o", exe], verbose)
+    return exe
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    if shutil.which("g++"):
+        print("built", LIB)

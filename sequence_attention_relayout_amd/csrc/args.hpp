@@ -1,0 +1,65 @@
+// Kernel argument blocks shared by the host plan and the HIP kernels.
+//
+// Plain C++ types only (no HIP headers), so the plan that fills them builds
+// and is unit-tested without a GPU.  Every block is passed to its kernel by
+// value through the kernarg segment; each stays well under 4 KiB.
+#pragma once
+#include <cstdint>
+
+namespace ulysses {
+
+constexpr int kMaxWorld = 8;
+constexpr int kMaxPieces = kMaxWorld * kMaxWorld;
+// A row of any shard is at most this many 16-byte vectors (512 KiB).  The
+// kernels split a block's vector range into rows with a 32-bit
+// multiply-high whose numerators stay below 2^16 under this bound.
+constexpr uint32_t kMaxRowVectors = 32768;
+
+// One (source rank j -> destination rank r) region of one batch plane: `rows`
+// rows of `vpr` 16-byte vectors, contiguous within each row on both sides.
+// Offsets and pitches are in 16-byte vectors.
+struct PieceArgs {
+    uint32_t nvec;        // rows * vpr
+    uint32_t vpr;         // vectors per row
+    uint32_t magic;       // floor(2^32 / vpr) + 1 when vpr >= 2, unused when vpr == 1
+    uint32_t src_pitch;   // row pitch in the source shard
+    uint32_t dst_pitch;   // row pitch in the destination shard
+    uint32_t src_off;     // first vector within the source plane
+    uint32_t dst_off;     // first vector within the destination plane
+    uint32_t src_row0;    // sequence position of the piece's first source row
+                          // (global position of row 0; used by the fused path)
+    uint8_t j, r;         // source and destination rank
+    uint8_t pad[2];
+};
+
+// Launch table for one relayout pass: grid.x walks the pieces' blocks, grid.y
+// the batch planes.  Block x belongs to the piece p with
+// blk_begin[p] <= x < blk_begin[p + 1]; unused entries hold 0xFFFFFFFF.
+struct RelayoutArgs {
+    const unsigned char *src[kMaxWorld];
+    unsigned char *dst[kMaxWorld];
+    uint64_t src_plane[kMaxWorld];   // vectors per batch plane of source shard j
+    uint64_t dst_plane[kMaxWorld];   // vectors per batch plane of destination shard r
+    uint32_t blk_begin[kMaxPieces];
+    PieceArgs piece[kMaxPieces];
+    uint32_t src_plane0;             // batch plane of grid.y == 0, source side
+    uint32_t dst_plane0;             // batch plane of grid.y == 0, destination side
+};
+
+// The fused QK-norm + RoPE mode-0 pass: the same piece table for q and k
+// (grid.z picks the tensor), plus the row-op parameters.
+struct FusedArgs {
+    const unsigned char *src[2][kMaxWorld];
+    unsigned char *dst[2][kMaxWorld];
+    uint64_t src_plane[kMaxWorld];
+    uint64_t dst_plane[kMaxWorld];
+    uint32_t blk_begin[kMaxPieces];
+    PieceArgs piece[kMaxPieces];
+    const float *gamma[2];
+    const float *rope_cos;
+    const float *rope_sin;
+    float eps;
+    uint32_t d;                      // head dimension (8 * lanes per head row)
+};
+
+}  // namespace ulysses

@@ -1,0 +1,268 @@
+// gfx950 (CDNA4) kernels of the Ulysses 4D relayout.
+//
+// The relayout is pure data movement: every byte is read once and written
+// once, so HBM bandwidth bounds it and there is no contraction for MFMA.
+// Each (source rank j -> destination rank r) piece is a set of rows that are
+// contiguous on both sides (at least d*elem_size >= 16 bytes, in practice
+// 640 B and up), so every lane moves whole 16-byte vectors with coalesced
+// loads and stores and no LDS staging is needed: the source and destination
+// strides already agree at 16-byte granularity.  The permutation itself is
+// only addressing, as the pages put it (fast-ulysses 0.1.0 introduction: the
+// sequence/head relayout is expressed as copy strides instead of separate
+// permute kernels).
+//
+// Work split: grid.x walks the blocks of all pieces (a piece table in the
+// kernarg segment, block ranges found with a branch-free scan), grid.y the
+// batch planes.  A block moves ULY_BLOCK * ULY_UNROLL consecutive vectors of
+// its piece; each thread issues ULY_UNROLL independent 16-byte loads before
+// its stores, ULY_BLOCK apart, so each load instruction of a wavefront
+// covers 1 KiB of contiguous memory.
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+#ifndef ULY_BLOCK
+#define ULY_BLOCK 256
+#endif
+#ifndef ULY_UNROLL
+#define ULY_UNROLL 4
+#endif
+#ifndef ULY_NT
+#define ULY_NT 1
+#endif
+#ifndef ULY_FUSED_UNROLL
+#define ULY_FUSED_UNROLL 2
+#endif
+
+namespace ulysses {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ u32x4 load16(const unsigned char *p) {
+    const u32x4 *q = reinterpret_cast<const u32x4 *>(p);
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(unsigned char *p, u32x4 v) {
+    u32x4 *q = reinterpret_cast<u32x4 *>(p);
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
+// The piece owning block x: blk_begin is ascending over used entries and
+// 0xFFFFFFFF past them, so the count of entries <= x (minus the first) is
+// the index.  Uniform across the block; the scan unrolls into scalar ops.
+__device__ __forceinline__ uint32_t find_piece(const uint32_t *blk_begin, uint32_t x) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxPieces; ++q) p += (blk_begin[q] <= x) ? 1u : 0u;
+    return p;
+}
+
+// Splits t (< 2^16) into (t / vpr, t % vpr) with one multiply-high; see
+// row_magic() in the plan for the bound.
+__device__ __forceinline__ uint32_t div_vpr(uint32_t t, uint32_t vpr, uint32_t magic) {
+    return vpr == 1 ? t : __umulhi(t, magic);
+}
+
+// --------------------------------------------------------------------------
+// Relayout (modes 0 and 1, and the window copy of the chunked mode)
+// --------------------------------------------------------------------------
+
+template <int BLOCK, int UNROLL, bool NT>
+__global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
+    const uint32_t x = blockIdx.x;
+    const uint32_t p = find_piece(a.blk_begin, x);
+    const PieceArgs pc = a.piece[p];
+    const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
+    // Row and column of the block's first vector (uniform); per-lane offsets
+    // from there stay below 2^16 (row length <= 32768 vectors).
+    const uint32_t row0 = s0 / pc.vpr;
+    const uint32_t col0 = s0 - row0 * pc.vpr;
+    const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
+    const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
+    const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
+    unsigned char *db = a.dst[pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
+
+    u32x4 v[UNROLL];
+    uint64_t doff[UNROLL];
+    bool ok[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+        const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
+        const uint32_t t = col0 + lin;
+        const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
+        const uint32_t col = t - dr * pc.vpr;
+        const uint32_t row = row0 + dr;
+        ok[k] = s0 + lin < pc.nvec;
+        const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
+        doff[k] = uint64_t(row) * pc.dst_pitch + col;
+        if (ok[k]) v[k] = load16<NT>(sb + soff * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k)
+        if (ok[k]) store16<NT>(db + doff[k] * 16, v[k]);
+}
+
+uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL; }
+
+hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
+                           hipStream_t stream) {
+    if (grid_x == 0 || planes == 0) return hipSuccess;
+    void *argv[] = {const_cast<RelayoutArgs *>(&a)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&relayout_kernel<ULY_BLOCK, ULY_UNROLL, ULY_NT != 0>),
+        dim3(grid_x, planes, 1), dim3(ULY_BLOCK, 1, 1), argv, 0, stream);
+}
+
+// --------------------------------------------------------------------------
+// Fused mode 0 with QK RMSNorm + RoPE (bf16 in, bf16 out, fp32 arithmetic)
+// --------------------------------------------------------------------------
+//
+// A head row of d bf16 elements is L = d/8 consecutive 16-byte vectors, so L
+// consecutive lanes hold one head row, lane l holding elements 8l..8l+7 and
+// rotary pairs 4l..4l+3.  Row boundaries fall on multiples of L in the flat
+// vector index and blocks start on multiples of L, so lane l of a thread is
+// threadIdx.x % L for every vector the thread touches.  The operation order
+// is fixed so the result is reproducible bit for bit:
+//   partial = fma chain over the lane's 8 squares, ascending;
+//   ss      = xor butterfly 1, 2, 4, ... over the L lanes, which equals the
+//             pairwise tree with adjacent pairing (fp32 + is commutative, so
+//             every lane of the group ends with the same bits);
+//   inv     = 1 / sqrt(ss / d + eps), correctly rounded division and sqrt;
+//   y       = (x * inv) * gamma;  rotation with separately rounded products.
+// The library is compiled with -ffp-contract=off so no product is fused.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two floats to bf16 (nearest even) and pack them, lo in bits 0..15.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const f32x2 f = {lo, hi};
+    const bf16x2 h = __builtin_convertvector(f, bf16x2);
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < L; m <<= 1) v = v + __shfl_xor(v, m, L);
+    return v;
+}
+
+template <int BLOCK, int UNROLL, int L>
+__global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
+    const uint32_t x = blockIdx.x;
+    const uint32_t tensor = blockIdx.z;
+    const uint32_t p = find_piece(a.blk_begin, x);
+    const PieceArgs pc = a.piece[p];
+    const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
+    const uint32_t row0 = s0 / pc.vpr;
+    const uint32_t col0 = s0 - row0 * pc.vpr;
+    const uint64_t plane = blockIdx.y;
+    const unsigned char *sb =
+        a.src[tensor][pc.j] + (plane * a.src_plane[pc.j] + pc.src_off) * 16;
+    unsigned char *db = a.dst[tensor][pc.r] + (plane * a.dst_plane[pc.r] + pc.dst_off) * 16;
+    const uint32_t lane = threadIdx.x & (L - 1);
+    const uint32_t half_d = a.d / 2;
+
+    // this lane's 8 gains
+    const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
+    const f32x4 g0 = gp[0], g1 = gp[1];
+    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float eps = a.eps;
+    const float dflt = float(a.d);
+
+    u32x4 xv[UNROLL];
+    f32x4 cv[UNROLL], sv[UNROLL];
+    uint64_t doff[UNROLL];
+    bool ok[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+        const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
+        const uint32_t t = col0 + lin;
+        const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
+        const uint32_t col = t - dr * pc.vpr;
+        const uint32_t row = row0 + dr;
+        ok[k] = s0 + lin < pc.nvec;
+        const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
+        doff[k] = uint64_t(row) * pc.dst_pitch + col;
+        // global sequence position of this source row
+        const uint64_t tab = uint64_t(pc.src_row0 + row) * half_d + 4 * lane;
+        xv[k] = u32x4{0, 0, 0, 0};
+        cv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (ok[k]) {
+            xv[k] = load16<true>(sb + soff * 16);
+            cv[k] = *reinterpret_cast<const f32x4 *>(a.rope_cos + tab);
+            sv[k] = *reinterpret_cast<const f32x4 *>(a.rope_sin + tab);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+        float xf[8];
+        xf[0] = bf16_lo(xv[k].x); xf[1] = bf16_hi(xv[k].x);
+        xf[2] = bf16_lo(xv[k].y); xf[3] = bf16_hi(xv[k].y);
+        xf[4] = bf16_lo(xv[k].z); xf[5] = bf16_hi(xv[k].z);
+        xf[6] = bf16_lo(xv[k].w); xf[7] = bf16_hi(xv[k].w);
+        float part = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(xf[i], xf[i], part);
+        const float ss = group_sum<L>(part);
+        // Plain '/' and __builtin_sqrtf: with hipcc's default of correctly
+        // rounded fp32 divide and sqrt these lower to the IEEE-exact
+        // sequences (div_scale/div_fmas/div_fixup; v_sqrt_f32 plus a one-ulp
+        // residual correction).  __fsqrt_rn would carry a 3-ulp fpmath bound.
+        const float ms = ss / dflt;
+        const float inv = 1.0f / __builtin_sqrtf(ms + eps);
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (xf[i] * inv) * g[i];
+        const float c[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
+        const float s[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float e0 = y[2 * q] * c[q];
+            const float e1 = y[2 * q + 1] * s[q];
+            const float e2 = y[2 * q] * s[q];
+            const float e3 = y[2 * q + 1] * c[q];
+            o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+        }
+        if (ok[k]) store16<true>(db + doff[k] * 16, u32x4{o[0], o[1], o[2], o[3]});
+    }
+}
+
+uint32_t fused_vectors_per_block() { return ULY_BLOCK * ULY_FUSED_UNROLL; }
+
+template <int L>
+static hipError_t launch_fused_l(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
+                                 hipStream_t stream) {
+    void *argv[] = {const_cast<FusedArgs *>(&a)};
+    return hipLaunchKernel(
+        reinterpret_cast<const void *>(&fused_kernel<ULY_BLOCK, ULY_FUSED_UNROLL, L>),
+        dim3(grid_x, planes, 2), dim3(ULY_BLOCK, 1, 1), argv, 0, stream);
+}
+
+hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
+                        hipStream_t stream) {
+    if (grid_x == 0 || planes == 0) return hipSuccess;
+    switch (a.d / 8) {
+    case 1: return launch_fused_l<1>(a, grid_x, planes, stream);
+    case 2: return launch_fused_l<2>(a, grid_x, planes, stream);
+    case 4: return launch_fused_l<4>(a, grid_x, planes, stream);
+    case 8: return launch_fused_l<8>(a, grid_x, planes, stream);
+    case 16: return launch_fused_l<16>(a, grid_x, planes, stream);
+    case 32: return launch_fused_l<32>(a, grid_x, planes, stream);
+    case 64: return launch_fused_l<64>(a, grid_x, planes, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ulysses

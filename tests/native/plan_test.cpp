@@ -1,0 +1,231 @@
+// Host-only test of the relayout plan (no GPU, no HIP headers).
+//
+// For many geometries it replays, on the CPU, the index arithmetic the
+// kernels perform for every (block, lane) of the launch tables the plan
+// fills, and checks that
+//   - every destination vector is written exactly once, and
+//   - it is read from the source address the definition names:
+//       mode 0: out_r[bi][S][h] = in_j[bi][S - seq_off_j][head_off_r + h],
+//       mode 1: out_r[bi][s][H] = in_j[bi][seq_off_r + s][H - head_off_j];
+//   - the window copy of the plane-at-a-time mode covers each destination
+//     plane once from the same offset in the window;
+//   - the fused path's lane of a vector within its head row is the thread's
+//     lane modulo d/8;
+//   - the multiply-high division by the row length is exact at every
+//     quotient boundary, hence everywhere (both sides are monotone).
+// Prints "OK <checks>" and exits 0, or a message and exits 1.
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "plan.hpp"
+
+using namespace ulysses;
+
+static long g_checks = 0;
+
+#define REQUIRE(c, ...)                                              \
+    do {                                                             \
+        ++g_checks;                                                  \
+        if (!(c)) {                                                  \
+            std::fprintf(stderr, "FAIL %s:%d: ", __FILE__, __LINE__); \
+            std::fprintf(stderr, __VA_ARGS__);                       \
+            std::fprintf(stderr, "\n");                              \
+            std::exit(1);                                            \
+        }                                                            \
+    } while (0)
+
+static uint32_t umulhi(uint32_t a, uint32_t b) {
+    return static_cast<uint32_t>((uint64_t(a) * b) >> 32);
+}
+
+// The kernels' mapping of (block x, plane y, linear lane lin) to vector
+// offsets; returns false when the lane is past its piece.
+struct Hit {
+    int j, r;
+    uint64_t src_vec, dst_vec;   // vector offsets from the shard bases
+    uint32_t col;
+};
+
+static bool replay(const RelayoutArgs &a, uint32_t vpb, uint32_t x, uint32_t y, uint32_t lin,
+                   Hit *h) {
+    uint32_t p = 0;
+    for (int q = 1; q < kMaxPieces; ++q) p += a.blk_begin[q] <= x ? 1u : 0u;
+    const PieceArgs &pc = a.piece[p];
+    const uint32_t s0 = (x - a.blk_begin[p]) * vpb;
+    const uint32_t row0 = s0 / pc.vpr;
+    const uint32_t col0 = s0 - row0 * pc.vpr;
+    const uint32_t t = col0 + lin;
+    if (t >= 65536u) {
+        std::fprintf(stderr, "numerator %u out of range\n", t);
+        std::exit(1);
+    }
+    const uint32_t dr = pc.vpr == 1 ? t : umulhi(t, pc.magic);
+    const uint32_t col = t - dr * pc.vpr;
+    const uint32_t row = row0 + dr;
+    if (s0 + lin >= pc.nvec) return false;
+    h->j = pc.j;
+    h->r = pc.r;
+    h->src_vec = (uint64_t(a.src_plane0) + y) * a.src_plane[pc.j] + pc.src_off +
+                 uint64_t(row) * pc.src_pitch + col;
+    h->dst_vec = (uint64_t(a.dst_plane0) + y) * a.dst_plane[pc.r] + pc.dst_off +
+                 uint64_t(row) * pc.dst_pitch + col;
+    h->col = col;
+    return true;
+}
+
+static void check_magic() {
+    for (uint32_t v = 2; v <= kMaxRowVectors; ++v) {
+        const uint32_t m = row_magic(v);
+        for (uint64_t k = 1; k * v <= 65536; ++k) {
+            const uint32_t lo = static_cast<uint32_t>(k * v - 1), hi = static_cast<uint32_t>(k * v);
+            REQUIRE(umulhi(lo, m) == k - 1, "magic vpr=%u t=%u", v, lo);
+            if (hi < 65536) REQUIRE(umulhi(hi, m) == k, "magic vpr=%u t=%u", v, hi);
+        }
+    }
+}
+
+static void check_geometry(int world, int64_t b, int64_t d, int dtype,
+                           const std::vector<int64_t> &S, const std::vector<int64_t> &H,
+                           uint32_t vpb) {
+    Plan p;
+    std::string msg;
+    const int rc = plan_build(&p, world, b, d, S.data(), H.data(), dtype, 1 << 30, &msg);
+    REQUIRE(rc == kOk, "plan_build failed: %s", msg.c_str());
+    const int64_t esz = dtype_size(dtype);
+    const int64_t hb = d * esz;
+    const int64_t n_global = p.n_global, s_global = p.s_global;
+    REQUIRE(hb % 16 == 0, "row alignment");
+    const int64_t hv = hb / 16;   // vectors per head row
+    for (int mode = 0; mode < 2; ++mode) {
+        for (int order = 0; order < 2; ++order) {
+            RelayoutArgs a;
+            const uint32_t gx = fill_relayout(p, mode, vpb, static_cast<PieceOrder>(order), &a);
+            std::vector<std::vector<int>> hits(world);
+            for (int r = 0; r < world; ++r)
+                hits[r].assign(static_cast<size_t>(b * p.mode[mode].dst_plane[r] / 16), 0);
+            for (uint32_t y = 0; y < b; ++y)
+                for (uint32_t x = 0; x < gx; ++x)
+                    for (uint32_t lin = 0; lin < vpb; ++lin) {
+                        Hit h;
+                        if (!replay(a, vpb, x, y, lin, &h)) continue;
+                        REQUIRE(h.dst_vec < hits[h.r].size(), "dst out of range");
+                        hits[h.r][h.dst_vec] += 1;
+                        // decode the destination vector and derive its source
+                        int64_t v = static_cast<int64_t>(h.dst_vec);
+                        int64_t want_j, want_src;
+                        if (mode == 0) {   // dst (b, s_global, H_r, hv)
+                            const int64_t e = v % hv; v /= hv;
+                            const int64_t hh = v % p.H[h.r]; v /= p.H[h.r];
+                            const int64_t Sg = v % s_global; const int64_t bi = v / s_global;
+                            int j = 0;
+                            while (!(p.seq_off[j] <= Sg && Sg < p.seq_off[j + 1])) ++j;
+                            want_j = j;
+                            want_src = ((bi * p.S[j] + (Sg - p.seq_off[j])) * n_global +
+                                        p.head_off[h.r] + hh) * hv + e;
+                        } else {           // dst (b, S_r, n_global, hv)
+                            const int64_t e = v % hv; v /= hv;
+                            const int64_t Hg = v % n_global; v /= n_global;
+                            const int64_t s = v % p.S[h.r]; const int64_t bi = v / p.S[h.r];
+                            int j = 0;
+                            while (!(p.head_off[j] <= Hg && Hg < p.head_off[j + 1])) ++j;
+                            want_j = j;
+                            want_src = ((bi * s_global + p.seq_off[h.r] + s) * p.H[j] +
+                                        (Hg - p.head_off[j])) * hv + e;
+                        }
+                        REQUIRE(h.j == want_j && static_cast<int64_t>(h.src_vec) == want_src,
+                                "mode %d W=%d: src (%d,%llu) want (%lld,%lld)", mode, world, h.j,
+                                (unsigned long long)h.src_vec, (long long)want_j,
+                                (long long)want_src);
+                        // fused lanes: lane within the head row == lin mod hv
+                        if (mode == 0 && (hv & (hv - 1)) == 0 && hv <= 64 && vpb % hv == 0)
+                            REQUIRE(int64_t(h.col % hv) == int64_t(lin % hv), "lane mapping");
+                    }
+            for (int r = 0; r < world; ++r)
+                for (size_t i = 0; i < hits[r].size(); ++i)
+                    REQUIRE(hits[r][i] == 1, "mode %d rank %d vector %zu written %d times", mode,
+                            r, i, hits[r][i]);
+        }
+        // window copy: plane y of dst r from window r plane 0, same offset
+        RelayoutArgs c;
+        const uint32_t gc = fill_window_copy(p, mode, vpb, &c);
+        for (uint32_t y = 0; y < b; ++y) {
+            c.src_plane0 = 0;
+            c.dst_plane0 = y;
+            std::vector<std::vector<int>> hits(world);
+            for (int r = 0; r < world; ++r)
+                hits[r].assign(static_cast<size_t>(p.mode[mode].dst_plane[r] / 16), 0);
+            for (uint32_t x = 0; x < gc; ++x)
+                for (uint32_t lin = 0; lin < vpb; ++lin) {
+                    Hit h;
+                    if (!replay(c, vpb, x, 0, lin, &h)) continue;
+                    REQUIRE(h.j == h.r, "copy crosses ranks");
+                    const uint64_t plane = p.mode[mode].dst_plane[h.r] / 16;
+                    REQUIRE(h.dst_vec == y * plane + h.src_vec, "copy offset");
+                    REQUIRE(h.src_vec < plane, "copy source past the window");
+                    hits[h.r][h.src_vec] += 1;
+                }
+            for (int r = 0; r < world; ++r)
+                for (size_t i = 0; i < hits[r].size(); ++i)
+                    REQUIRE(hits[r][i] == 1, "copy coverage");
+        }
+    }
+}
+
+static void check_errors() {
+    Plan p;
+    std::string m;
+    const int64_t s2[2] = {4, 4}, h2[2] = {2, 2};
+    REQUIRE(plan_build(&p, 0, 1, 8, s2, h2, 0, 0, &m) == kEInval, "world 0");
+    REQUIRE(plan_build(&p, 9, 1, 8, s2, h2, 0, 0, &m) == kEInval, "world 9");
+    REQUIRE(plan_build(&p, 2, 0, 8, s2, h2, 0, 0, &m) == kEInval, "b 0");
+    REQUIRE(plan_build(&p, 2, 1, 4, s2, h2, 0, 0, &m) == kEAlign, "d*esz 8");
+    REQUIRE(plan_build(&p, 2, 1, 8, s2, h2, 9, 0, &m) == kEDtype, "dtype");
+    REQUIRE(plan_build(&p, 2, 1, 8, s2, h2, 3, 0, &m) == kEAlign, "fp8 d=8");
+    const int64_t neg[2] = {-1, 5}, zero[2] = {0, 0};
+    REQUIRE(plan_build(&p, 2, 1, 8, neg, h2, 0, 0, &m) == kEInval, "negative split");
+    REQUIRE(plan_build(&p, 2, 1, 8, zero, h2, 0, 0, &m) == kEInval, "zero sum");
+    const int64_t big[2] = {1024, 1025};
+    REQUIRE(plan_build(&p, 2, 1, 128, s2, big, 0, 0, &m) == kEInval, "row over 512 KiB");
+    REQUIRE(plan_build(&p, 2, 1, 8, s2, h2, 0, -1, &m) == kEInval, "negative cap");
+    // the FastVideo geometry: 896,000,000 bytes per rank per plane
+    const int64_t s4[4] = {62500, 62500, 62500, 62500}, h4[4] = {14, 14, 14, 14};
+    REQUIRE(plan_build(&p, 4, 3, 128, s4, h4, 0, 1 << 30, &m) == kOk, "fastvideo plan");
+    REQUIRE(p.mode[0].window_bytes == 896000000 && p.mode[1].window_bytes == 896000000,
+            "window bytes");
+}
+
+int main() {
+    check_magic();
+    check_errors();
+    std::mt19937_64 rng(12345);
+    const uint32_t vpbs[] = {64, 256, 1024, 2048};
+    const int dtypes[] = {0, 2, 3, 5};
+    for (int it = 0; it < 160; ++it) {
+        const int world = 1 + static_cast<int>(rng() % 8);
+        const int dtype = dtypes[rng() % 4];
+        const int64_t esz = dtype_size(dtype);
+        const int64_t unit = 16 / esz;   // smallest legal d
+        const int64_t d = unit * (1 + static_cast<int64_t>(rng() % 3));
+        const int64_t b = 1 + static_cast<int64_t>(rng() % 3);
+        std::vector<int64_t> S(world), H(world);
+        int64_t ss = 0, hs = 0;
+        for (int r = 0; r < world; ++r) {
+            S[r] = static_cast<int64_t>(rng() % 40) - (it % 3 == 0 ? 5 : 0);
+            if (S[r] < 0) S[r] = 0;
+            H[r] = static_cast<int64_t>(rng() % 5);
+            ss += S[r];
+            hs += H[r];
+        }
+        if (ss == 0) S[0] = 3;
+        if (hs == 0) H[world - 1] = 2;
+        check_geometry(world, b, d, dtype, S, H, vpbs[rng() % 4]);
+    }
+    // long rows: row length near the 32768-vector limit, vpr == 1 rows
+    check_geometry(2, 1, 2048, 2, {3, 2}, {40, 24}, 2048);
+    check_geometry(3, 2, 16, 5, {5, 1, 7}, {1, 1, 1}, 64);
+    std::printf("OK %ld\n", g_checks);
+    return 0;
+}

@@ -1,0 +1,178 @@
+"""Host-only checks of libulysses.so: no GPU, nothing is launched.
+
+- the library loads and exports every function include/ulysses.h declares;
+- the plan (shapes, window bytes, byte counts) agrees with the oracle on
+  random geometries and with the value the FastVideo page prints;
+- every validation error is returned before anything is enqueued (all
+  calls here fail validation, so fake device addresses are never touched);
+- the library's rotary table equals the oracle's bit for bit;
+- the native plan test replays the kernels' index math over every vector.
+"""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from sequence_attention_relayout_amd import build as ulybuild
+from sequence_attention_relayout_amd import ulysses as U
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if not os.path.exists(U.LIB_PATH):
+        ulybuild.build()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ulysses.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ulysses_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 10
+    lib = U.library()
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ulysses.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", U.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ulysses_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_native_plan_replay():
+    exe = ulybuild.build_plan_test()
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.startswith("OK")
+
+
+def rand_geom(rng):
+    world = int(rng.integers(1, 9))
+    seq = [int(v) for v in rng.integers(0, 50, world)]
+    head = [int(v) for v in rng.integers(0, 6, world)]
+    if sum(seq) == 0:
+        seq[0] = 1
+    if sum(head) == 0:
+        head[-1] = 1
+    return world, int(rng.integers(1, 4)), seq, head
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_plan_agrees_with_oracle(seed):
+    rng = np.random.default_rng(seed)
+    world, b, seq, head = rand_geom(rng)
+    dt = ["bf16", "fp32", "fp8_e4m3", "int8", "fp16", "uint8", "fp8_e5m2"][seed % 7]
+    esz = {"bf16": 2, "fp16": 2, "fp32": 4}.get(dt, 1)
+    d = (16 // esz) * int(rng.integers(1, 5))
+    plan = U.ulysses_plan_create(world, b, d, seq, head, dt)
+    for mode in (0, 1):
+        for r in range(world):
+            for is_dst in (False, True):
+                assert U.ulysses_plan_shape(plan, mode, r, is_dst) == \
+                    oracle.shape(mode, b, d, seq, head, r, is_dst)
+        assert U.ulysses_plan_window_bytes(plan, mode) == \
+            oracle.window_bytes(mode, d, esz, seq, head)
+        assert U.ulysses_plan_bytes(plan, mode) == 2 * b * sum(seq) * sum(head) * d * esz
+
+
+def test_fastvideo_plane_bytes(golden):
+    g = golden["fastvideo_window"]
+    w = g["world"]
+    plan = U.ulysses_plan_create(w, 3, g["d"], [g["s_global"] // w] * w,
+                                 [g["n_global"] // w] * w, "bf16", g["window_cap_bytes"])
+    for mode in (0, 1):
+        assert U.ulysses_plan_window_bytes(plan, mode) == g["bytes_per_plane"]
+
+
+def test_page_limits(golden):
+    lim = golden["limits_021"]
+    for w in range(lim["world_min"], lim["world_max"] + 1):
+        U.ulysses_plan_create(w, 1, 8, [1] * w, [1] * w, "bf16")
+    for w in (lim["world_min"] - 1, lim["world_max"] + 1):
+        with pytest.raises(U.UlyssesError) as e:
+            U.ulysses_plan_create(w, 1, 8, [1] * w, [1] * w, "bf16")
+        assert e.value.code == -1
+    for dt, m in lim["min_d_multiple"].items():
+        U.ulysses_plan_create(1, 1, m, [1], [1], dt)
+        if m > 1:
+            with pytest.raises(U.UlyssesError) as e:
+                U.ulysses_plan_create(1, 1, m // 2, [1], [1], dt)
+            assert e.value.code == -2
+
+
+def expect(code, fn, *args):
+    with pytest.raises(U.UlyssesError) as e:
+        fn(*args)
+    assert e.value.code == code, str(e.value)
+    return str(e.value)
+
+
+def test_plan_errors():
+    expect(-1, U.ulysses_plan_create, 2, 0, 8, [1, 1], [1, 1], "bf16")
+    expect(-1, U.ulysses_plan_create, 2, 1, 8, [-1, 2], [1, 1], "bf16")
+    expect(-1, U.ulysses_plan_create, 2, 1, 8, [0, 0], [1, 1], "bf16")
+    expect(-1, U.ulysses_plan_create, 2, 1, 8, [1, 1], [0, 0], "bf16")
+    expect(-2, U.ulysses_plan_create, 2, 1, 4, [1, 1], [1, 1], "bf16")
+    expect(-3, U.ulysses_plan_create, 2, 1, 8, [1, 1], [1, 1], 17)
+    msg = expect(-1, U.ulysses_plan_create, 1, 1, 4096, [1], [33], "fp32")
+    assert "512 KiB" in msg
+    assert "512 KiB" in U.ulysses_last_error()
+
+
+# Fake, never-dereferenced device addresses: each call below fails
+# validation before any launch.
+BASE = 1 << 40
+
+
+def fake(n, stride=1 << 32, off=0):
+    return [BASE + off + i * stride for i in range(n)]
+
+
+def test_call_errors_before_launch():
+    plan = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16")
+    src, dst = fake(2), fake(2, off=1 << 36)
+    expect(-1, U.ulysses_a2a_4d, plan, 2, src, dst, 0)                       # bad mode
+    expect(-1, U.ulysses_a2a_4d, plan, 0, [src[0], 0], dst, 0)               # null src
+    expect(-2, U.ulysses_a2a_4d, plan, 0, [src[0] + 8, src[1]], dst, 0)      # misaligned
+    expect(-2, U.ulysses_a2a_4d, plan, 1, src, [dst[0], dst[1] + 4], 0)
+    expect(-5, U.ulysses_a2a_4d, plan, 0, src, [dst[0], src[1] + 16], 0)     # dst on a src
+    expect(-5, U.ulysses_a2a_4d, plan, 0, src, [dst[0], dst[0] + 16], 0)     # dst on a dst
+    # chunked: no cap, window too small for the cap, window overlapping
+    expect(-1, U.ulysses_a2a_4d_chunked, plan, 0, src, dst, fake(2, off=1 << 37), 0)
+    small = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16", 64)
+    expect(-4, U.ulysses_a2a_4d_chunked, small, 0, src, dst, fake(2, off=1 << 37), 0)
+    capped = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16", 1 << 20)
+    expect(-5, U.ulysses_a2a_4d_chunked, capped, 0, src, dst, [src[0], dst[1] + (1 << 30)], 0)
+    expect(-5, U.ulysses_a2a_4d_chunked, capped, 1, src, dst,
+           [BASE + (1 << 38), BASE + (1 << 38) + 16], 0)
+    # fused: bf16 only, power-of-two d/8, non-null tables, eps >= 0
+    f32 = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "fp32")
+    g, t = BASE + (1 << 39), BASE + (1 << 39) + (1 << 30)
+    expect(-3, U.ulysses_a2a_4d_qknorm_rope, f32, src, dst, fake(2, off=7 << 33),
+           fake(2, off=15 << 33), g, g + 64, 1e-6, t, t + (1 << 28), 0)
+    d24 = U.ulysses_plan_create(2, 1, 24, [3, 4], [1, 2], "bf16")
+    expect(-1, U.ulysses_a2a_4d_qknorm_rope, d24, src, dst, fake(2, off=7 << 33),
+           fake(2, off=15 << 33), g, g + 128, 1e-6, t, t + (1 << 28), 0)
+    expect(-1, U.ulysses_a2a_4d_qknorm_rope, plan, src, dst, fake(2, off=7 << 33),
+           fake(2, off=15 << 33), g, g + 64, -1.0, t, t + (1 << 28), 0)
+    expect(-1, U.ulysses_a2a_4d_qknorm_rope, plan, src, dst, fake(2, off=7 << 33),
+           fake(2, off=15 << 33), g, g + 64, 1e-6, 0, t + (1 << 28), 0)
+    expect(-5, U.ulysses_a2a_4d_qknorm_rope, plan, src, dst, fake(2, off=7 << 33),
+           [g, BASE + (15 << 33)], g + 64, g + 128, 1e-6, t, t + (1 << 28), 0)
+
+
+def test_rope_table_matches_oracle_bitwise():
+    for theta, s, d in [(10000.0, 75600, 128), (500000.0, 1000, 64), (10000.0, 3, 8)]:
+        c, sn = U.ulysses_rope_table(theta, s, d)
+        oc, osn = oracle.rope_table(theta, s, d)
+        assert c.view(np.uint32).tobytes() == oc.view(np.uint32).tobytes()
+        assert sn.view(np.uint32).tobytes() == osn.view(np.uint32).tobytes()
+    expect(-1, U.ulysses_rope_table, 0.0, 4, 8)
+    expect(-1, U.ulysses_rope_table, 10000.0, 4, 7)
