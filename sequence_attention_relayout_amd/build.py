@@ -40,7 +40,7 @@ def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
     objs = []
     for src in ("plan.cpp", "capi.cpp"):
         obj = os.path.join(build_dir, src.replace(".cpp", ".o"))
-        _run(["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run(["g++", *HOST_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     kobj = os.path.join(build_dir, "kernels.o")
     _run([hipcc, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj],

@@ -44,6 +44,14 @@ struct RelayoutArgs {
     PieceArgs piece[kMaxPieces];
     uint32_t src_plane0;             // batch plane of grid.y == 0, source side
     uint32_t dst_plane0;             // batch plane of grid.y == 0, destination side
+    // Row-band traversal (fill_relayout_bands): the pieces sharing one
+    // row-sharded shard g (source j in mode 0, destination r in mode 1) sit
+    // at piece[g * world + k]; their blocks interleave band by band: block
+    // grp_begin[g] + band * world + k moves rows [band*band_rows,
+    // (band+1)*band_rows) of piece (g, k).  Unused entries hold 0xFFFFFFFF.
+    uint32_t grp_begin[kMaxWorld];
+    uint32_t world;
+    uint32_t band_rows;
 };
 
 // The fused QK-norm + RoPE mode-0 pass: the same piece table for q and k

@@ -18,6 +18,25 @@ struct ulysses_plan {
     ulysses::Plan p;
 };
 
+#ifndef ULY_ORDER
+#define ULY_ORDER 0
+#endif
+// Order in which the pieces of a relayout take consecutive blocks.
+static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrder>(ULY_ORDER);
+
+#ifndef ULY_BAND
+#define ULY_BAND 256
+#endif
+
+// Launch table of one relayout pass: row bands of about ULY_BAND vectors
+// when ULY_BAND > 0, else flat blocks in kRelayoutOrder.
+static uint32_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
+    if (ULY_BAND > 0)
+        return ulysses::fill_relayout_bands(p, mode, ulysses::band_rows_for(p, mode, ULY_BAND), a);
+    return ulysses::fill_relayout(p, mode, ulysses::relayout_vectors_per_block(), kRelayoutOrder,
+                                  a);
+}
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -186,8 +205,7 @@ int ulysses_a2a_4d(const ulysses_plan *plan, int mode, const void *const *src,
         rc = check_overlap(ranges);
         if (rc) return rc;
         ulysses::RelayoutArgs a;
-        const uint32_t gx = ulysses::fill_relayout(p, mode, ulysses::relayout_vectors_per_block(),
-                                                   ulysses::kDstMajor, &a);
+        const uint32_t gx = relayout_table(p, mode, &a);
         set_pointers(p, src, dst, &a);
         return launch_status(
             ulysses::launch_relayout(a, gx, static_cast<uint32_t>(p.b), stream), "relayout");
@@ -223,7 +241,7 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
 
         ulysses::RelayoutArgs scatter, copy;
         const uint32_t vpb = ulysses::relayout_vectors_per_block();
-        const uint32_t gs = ulysses::fill_relayout(p, mode, vpb, ulysses::kDstMajor, &scatter);
+        const uint32_t gs = relayout_table(p, mode, &scatter);
         const uint32_t gc = ulysses::fill_window_copy(p, mode, vpb, &copy);
         for (int r = 0; r < p.world; ++r) {
             scatter.src[r] = static_cast<const unsigned char *>(src[r]);

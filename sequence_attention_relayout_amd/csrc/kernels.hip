@@ -21,14 +21,30 @@
 
 #include "kernels.hpp"
 
+// Launch shape, chosen by measurement on MI355X (W=8, 75,600 tokens, bf16):
+// 128-thread blocks moving 2 vectors per thread in row bands of about 256
+// vectors beat larger blocks, deeper unrolls, longer bands and capped
+// occupancy.
 #ifndef ULY_BLOCK
-#define ULY_BLOCK 256
+#define ULY_BLOCK 128
 #endif
 #ifndef ULY_UNROLL
-#define ULY_UNROLL 4
+#define ULY_UNROLL 2
 #endif
+#ifndef ULY_XCD
+#define ULY_XCD 0
+#endif
+// Dynamic LDS bytes requested per relayout block (unused by the kernel);
+// a non-zero value caps how many blocks share a CU.
+#ifndef ULY_LDS
+#define ULY_LDS 0
+#endif
+#ifndef ULY_ITERS
+#define ULY_ITERS 1
+#endif
+// bit 0: non-temporal loads, bit 1: non-temporal stores
 #ifndef ULY_NT
-#define ULY_NT 1
+#define ULY_NT 3
 #endif
 #ifndef ULY_FUSED_UNROLL
 #define ULY_FUSED_UNROLL 2
@@ -73,50 +89,118 @@ __device__ __forceinline__ uint32_t div_vpr(uint32_t t, uint32_t vpr, uint32_t m
 // Relayout (modes 0 and 1, and the window copy of the chunked mode)
 // --------------------------------------------------------------------------
 
-template <int BLOCK, int UNROLL, bool NT>
+// Blocks are dispatched round-robin over the 8 XCDs (block x to XCD x % 8).
+// With ULY_XCD the block index is permuted so that XCD k walks the k-th
+// contiguous eighth of the blocks (a bijection for any grid size).
+__device__ __forceinline__ uint32_t xcd_block(uint32_t x, uint32_t n) {
+#if ULY_XCD
+    const uint32_t q = n / 8, r = n % 8, xcd = x % 8, local = x / 8;
+    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
+#else
+    (void)n;
+    return x;
+#endif
+}
+
+template <int BLOCK, int UNROLL, int ITERS, bool NTL, bool NTS>
 __global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
-    const uint32_t x = blockIdx.x;
+    const uint32_t x = xcd_block(blockIdx.x, gridDim.x);
     const uint32_t p = find_piece(a.blk_begin, x);
     const PieceArgs pc = a.piece[p];
-    const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
-    // Row and column of the block's first vector (uniform); per-lane offsets
-    // from there stay below 2^16 (row length <= 32768 vectors).
-    const uint32_t row0 = s0 / pc.vpr;
-    const uint32_t col0 = s0 - row0 * pc.vpr;
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
     const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
     unsigned char *db = a.dst[pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
 
-    u32x4 v[UNROLL];
-    uint64_t doff[UNROLL];
-    bool ok[UNROLL];
+    for (int it = 0; it < ITERS; ++it) {
+        const uint32_t s0 = ((x - a.blk_begin[p]) * ITERS + it) * uint32_t(BLOCK * UNROLL);
+        if (s0 >= pc.nvec) break;
+        // Row and column of the chunk's first vector (uniform); per-lane
+        // offsets from there stay below 2^16 (row length <= 32768 vectors).
+        const uint32_t row0 = s0 / pc.vpr;
+        const uint32_t col0 = s0 - row0 * pc.vpr;
+        u32x4 v[UNROLL];
+        uint64_t doff[UNROLL];
+        bool ok[UNROLL];
 #pragma unroll
-    for (int k = 0; k < UNROLL; ++k) {
-        const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
-        const uint32_t t = col0 + lin;
-        const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
-        const uint32_t col = t - dr * pc.vpr;
-        const uint32_t row = row0 + dr;
-        ok[k] = s0 + lin < pc.nvec;
-        const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
-        doff[k] = uint64_t(row) * pc.dst_pitch + col;
-        if (ok[k]) v[k] = load16<NT>(sb + soff * 16);
+        for (int k = 0; k < UNROLL; ++k) {
+            const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
+            const uint32_t t = col0 + lin;
+            const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
+            const uint32_t col = t - dr * pc.vpr;
+            const uint32_t row = row0 + dr;
+            ok[k] = s0 + lin < pc.nvec;
+            const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
+            doff[k] = uint64_t(row) * pc.dst_pitch + col;
+            if (ok[k]) v[k] = load16<NTL>(sb + soff * 16);
+        }
+#pragma unroll
+        for (int k = 0; k < UNROLL; ++k)
+            if (ok[k]) store16<NTS>(db + doff[k] * 16, v[k]);
     }
-#pragma unroll
-    for (int k = 0; k < UNROLL; ++k)
-        if (ok[k]) store16<NT>(db + doff[k] * 16, v[k]);
 }
 
-uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL; }
+// Row-band traversal: block x moves one band of rows of one piece; the W
+// pieces that share a row-sharded shard take consecutive blocks band by
+// band, so blocks running side by side sweep whole contiguous rows of that
+// shard and W contiguous streams of the head-sharded side.
+template <int BLOCK, int UNROLL, bool NTL, bool NTS>
+__global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs a) {
+    const uint32_t x = xcd_block(blockIdx.x, gridDim.x);
+    uint32_t g = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
+    const uint32_t local = x - a.grp_begin[g];
+    const uint32_t band = local / a.world;
+    const uint32_t k = local - band * a.world;
+    const PieceArgs pc = a.piece[g * a.world + k];
+    const uint32_t begin = band * a.band_rows * pc.vpr;
+    const uint32_t end = min(begin + a.band_rows * pc.vpr, pc.nvec);
+    const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
+    const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
+    const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
+    unsigned char *db = a.dst[pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
+
+    for (uint32_t s0 = begin; s0 < end; s0 += uint32_t(BLOCK * UNROLL)) {
+        const uint32_t row0 = s0 / pc.vpr;
+        const uint32_t col0 = s0 - row0 * pc.vpr;
+        u32x4 v[UNROLL];
+        uint64_t doff[UNROLL];
+        bool ok[UNROLL];
+#pragma unroll
+        for (int kk = 0; kk < UNROLL; ++kk) {
+            const uint32_t lin = threadIdx.x + uint32_t(kk * BLOCK);
+            const uint32_t t = col0 + lin;
+            const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
+            const uint32_t col = t - dr * pc.vpr;
+            const uint32_t row = row0 + dr;
+            ok[kk] = s0 + lin < end;
+            const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
+            doff[kk] = uint64_t(row) * pc.dst_pitch + col;
+            if (ok[kk]) v[kk] = load16<NTL>(sb + soff * 16);
+        }
+#pragma unroll
+        for (int kk = 0; kk < UNROLL; ++kk)
+            if (ok[kk]) store16<NTS>(db + doff[kk] * 16, v[kk]);
+    }
+}
+
+uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL * ULY_ITERS; }
 
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
                            hipStream_t stream) {
     if (grid_x == 0 || planes == 0) return hipSuccess;
     void *argv[] = {const_cast<RelayoutArgs *>(&a)};
-    return hipLaunchKernel(
-        reinterpret_cast<const void *>(&relayout_kernel<ULY_BLOCK, ULY_UNROLL, ULY_NT != 0>),
-        dim3(grid_x, planes, 1), dim3(ULY_BLOCK, 1, 1), argv, 0, stream);
+    const void *fn =
+        a.band_rows != 0
+            ? reinterpret_cast<const void *>(
+                  &relayout_band_kernel<ULY_BLOCK, ULY_UNROLL, (ULY_NT & 1) != 0,
+                                        (ULY_NT & 2) != 0>)
+            : reinterpret_cast<const void *>(
+                  &relayout_kernel<ULY_BLOCK, ULY_UNROLL, ULY_ITERS, (ULY_NT & 1) != 0,
+                                   (ULY_NT & 2) != 0>);
+    return hipLaunchKernel(fn, dim3(grid_x, planes, 1), dim3(ULY_BLOCK, 1, 1), argv, ULY_LDS,
+                           stream);
 }
 
 // --------------------------------------------------------------------------

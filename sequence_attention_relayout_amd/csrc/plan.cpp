@@ -155,6 +155,43 @@ static void fill_piece_args(const Piece &pc, PieceArgs *o) {
 static void clear_table(RelayoutArgs *a) {
     std::memset(a, 0, sizeof *a);
     for (int q = 0; q < kMaxPieces; ++q) a->blk_begin[q] = 0xFFFFFFFFu;
+    for (int q = 0; q < kMaxWorld; ++q) a->grp_begin[q] = 0xFFFFFFFFu;
+}
+
+uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors) {
+    int64_t widest = 1;
+    for (int q = 0; q < p.world * p.world; ++q) {
+        const int64_t vpr = p.mode[mode].piece[q].row_bytes / 16;
+        if (vpr > widest) widest = vpr;
+    }
+    const int64_t t = target_vectors / widest;
+    return static_cast<uint32_t>(t < 1 ? 1 : t);
+}
+
+uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a) {
+    clear_table(a);
+    const ModeGeom &g = p.mode[mode];
+    for (int r = 0; r < p.world; ++r) {
+        a->src_plane[r] = static_cast<uint64_t>(g.src_plane[r] / 16);
+        a->dst_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
+    }
+    a->world = static_cast<uint32_t>(p.world);
+    a->band_rows = band_rows;
+    uint64_t blocks = 0;
+    for (int grp = 0; grp < p.world; ++grp) {
+        // every piece of the group has S_grp rows (mode 0: source rank j =
+        // grp; mode 1: destination rank r = grp)
+        const int64_t rows = p.S[grp];
+        const int64_t bands = (rows + band_rows - 1) / band_rows;
+        for (int k = 0; k < p.world; ++k) {
+            const int j = mode == 0 ? grp : k;
+            const int r = mode == 0 ? k : grp;
+            fill_piece_args(g.piece[j * p.world + r], &a->piece[grp * p.world + k]);
+        }
+        a->grp_begin[grp] = static_cast<uint32_t>(blocks);
+        blocks += static_cast<uint64_t>(bands) * p.world;
+    }
+    return static_cast<uint32_t>(blocks);
 }
 
 uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,

@@ -80,6 +80,14 @@ enum PieceOrder : int {
 uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
                        RelayoutArgs *a);
 
+// Row-band launch table of one relayout pass of `mode` (see
+// RelayoutArgs::grp_begin): bands of `band_rows` rows.  Returns grid.x.
+uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a);
+
+// Band height so that one band of the widest piece moves about
+// `target_vectors` 16-byte vectors (at least one row).
+uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
+
 // Launch table of the plane copy from the W windows (one destination plane
 // each) into the destination shards: one piece per rank whose source and
 // destination rows have the same pitch.

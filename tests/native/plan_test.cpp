@@ -16,6 +16,7 @@
 // Prints "OK <checks>" and exits 0, or a message and exits 1.
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <random>
 #include <vector>
@@ -76,6 +77,41 @@ static bool replay(const RelayoutArgs &a, uint32_t vpb, uint32_t x, uint32_t y, 
     return true;
 }
 
+// The band kernel's mapping: block x, chunk-relative lane `lin` of chunk
+// `c`; returns false when the lane (or the whole chunk) is past the band.
+static bool replay_band(const RelayoutArgs &a, uint32_t chunk, uint32_t x, uint32_t y,
+                        uint32_t c, uint32_t lin, Hit *h) {
+    uint32_t g = 0;
+    for (int q = 1; q < kMaxWorld; ++q) g += a.grp_begin[q] <= x ? 1u : 0u;
+    const uint32_t local = x - a.grp_begin[g];
+    const uint32_t band = local / a.world;
+    const uint32_t k = local - band * a.world;
+    const PieceArgs &pc = a.piece[g * a.world + k];
+    const uint32_t begin = band * a.band_rows * pc.vpr;
+    const uint32_t end = std::min(begin + a.band_rows * pc.vpr, pc.nvec);
+    const uint32_t s0 = begin + c * chunk;
+    if (s0 >= end) return false;
+    const uint32_t row0 = s0 / pc.vpr;
+    const uint32_t col0 = s0 - row0 * pc.vpr;
+    const uint32_t t = col0 + lin;
+    if (t >= 65536u) {
+        std::fprintf(stderr, "numerator %u out of range\n", t);
+        std::exit(1);
+    }
+    const uint32_t dr = pc.vpr == 1 ? t : umulhi(t, pc.magic);
+    const uint32_t col = t - dr * pc.vpr;
+    const uint32_t row = row0 + dr;
+    if (s0 + lin >= end) return false;
+    h->j = pc.j;
+    h->r = pc.r;
+    h->src_vec = (uint64_t(a.src_plane0) + y) * a.src_plane[pc.j] + pc.src_off +
+                 uint64_t(row) * pc.src_pitch + col;
+    h->dst_vec = (uint64_t(a.dst_plane0) + y) * a.dst_plane[pc.r] + pc.dst_off +
+                 uint64_t(row) * pc.dst_pitch + col;
+    h->col = col;
+    return true;
+}
+
 static void check_magic() {
     for (uint32_t v = 2; v <= kMaxRowVectors; ++v) {
         const uint32_t m = row_magic(v);
@@ -100,17 +136,31 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
     REQUIRE(hb % 16 == 0, "row alignment");
     const int64_t hv = hb / 16;   // vectors per head row
     for (int mode = 0; mode < 2; ++mode) {
-        for (int order = 0; order < 2; ++order) {
+        // traversals 0, 1: flat in both piece orders; 2, 3: row bands of
+        // two heights, with chunks of vpb vectors
+        for (int trav = 0; trav < 4; ++trav) {
             RelayoutArgs a;
-            const uint32_t gx = fill_relayout(p, mode, vpb, static_cast<PieceOrder>(order), &a);
+            uint32_t gx, nchunks = 1;
+            if (trav < 2) {
+                gx = fill_relayout(p, mode, vpb, static_cast<PieceOrder>(trav), &a);
+            } else {
+                const uint32_t rows = trav == 2 ? band_rows_for(p, mode, vpb) : 3;
+                gx = fill_relayout_bands(p, mode, rows, &a);
+                uint32_t widest = 1;
+                for (int q = 0; q < kMaxPieces; ++q) widest = std::max(widest, a.piece[q].vpr);
+                nchunks = (rows * widest + vpb - 1) / vpb;
+            }
             std::vector<std::vector<int>> hits(world);
             for (int r = 0; r < world; ++r)
                 hits[r].assign(static_cast<size_t>(b * p.mode[mode].dst_plane[r] / 16), 0);
             for (uint32_t y = 0; y < b; ++y)
                 for (uint32_t x = 0; x < gx; ++x)
+                    for (uint32_t c = 0; c < nchunks; ++c)
                     for (uint32_t lin = 0; lin < vpb; ++lin) {
                         Hit h;
-                        if (!replay(a, vpb, x, y, lin, &h)) continue;
+                        const bool in = trav < 2 ? replay(a, vpb, x, y, lin, &h)
+                                                 : replay_band(a, vpb, x, y, c, lin, &h);
+                        if (!in) continue;
                         REQUIRE(h.dst_vec < hits[h.r].size(), "dst out of range");
                         hits[h.r][h.dst_vec] += 1;
                         // decode the destination vector and derive its source
@@ -140,13 +190,14 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
                                 (unsigned long long)h.src_vec, (long long)want_j,
                                 (long long)want_src);
                         // fused lanes: lane within the head row == lin mod hv
-                        if (mode == 0 && (hv & (hv - 1)) == 0 && hv <= 64 && vpb % hv == 0)
+                        if (trav < 2 && mode == 0 && (hv & (hv - 1)) == 0 && hv <= 64 &&
+                            vpb % hv == 0)
                             REQUIRE(int64_t(h.col % hv) == int64_t(lin % hv), "lane mapping");
                     }
             for (int r = 0; r < world; ++r)
                 for (size_t i = 0; i < hits[r].size(); ++i)
-                    REQUIRE(hits[r][i] == 1, "mode %d rank %d vector %zu written %d times", mode,
-                            r, i, hits[r][i]);
+                    REQUIRE(hits[r][i] == 1, "trav %d mode %d rank %d vector %zu written %d times",
+                            trav, mode, r, i, hits[r][i]);
         }
         // window copy: plane y of dst r from window r plane 0, same offset
         RelayoutArgs c;
