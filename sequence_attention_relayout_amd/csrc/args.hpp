@@ -49,13 +49,19 @@ struct RelayoutArgs {
     // at piece[g * world + k]; their blocks interleave band by band: block
     // grp_begin[g] + band * world + k moves rows [band*band_rows,
     // (band+1)*band_rows) of piece (g, k).  Unused entries hold 0xFFFFFFFF.
+    // With band_vecs != 0 a band is instead band_vecs consecutive vectors of
+    // the piece (the same rows across the group when its rows are equally
+    // wide); a block whose band starts past its piece does nothing.
     uint32_t grp_begin[kMaxWorld];
     uint32_t world;
     uint32_t band_rows;
+    uint32_t band_vecs;
 };
 
 // The fused QK-norm + RoPE mode-0 pass: the same piece table for q and k
-// (grid.z picks the tensor), plus the row-op parameters.
+// (grid.z picks the tensor), plus the row-op parameters.  Vector counts,
+// offsets and pitches of the pieces are in units of the kernel's vectors per
+// lane (see to_units in the plan).
 struct FusedArgs {
     const unsigned char *src[2][kMaxWorld];
     unsigned char *dst[2][kMaxWorld];
@@ -67,7 +73,8 @@ struct FusedArgs {
     const float *rope_cos;
     const float *rope_sin;
     float eps;
-    uint32_t d;                      // head dimension (8 * lanes per head row)
+    float inv_d;                     // 1/d, exact (d is a power of two)
+    uint32_t d;                      // head dimension
 };
 
 }  // namespace ulysses

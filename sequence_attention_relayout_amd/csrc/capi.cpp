@@ -24,13 +24,23 @@ struct ulysses_plan {
 // Order in which the pieces of a relayout take consecutive blocks.
 static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrder>(ULY_ORDER);
 
+// Launch table choice, by measurement on MI355X (W=8, 75,600 tokens, bf16,
+// GB/s per mode-0 + mode-1 step): bands of 256 vectors interleaved over the
+// group (~6.18 TB/s) beat row bands of ~256 vectors (~6.05), the flat walk
+// (~5.86) and longer bands (512 vectors: ~5.93).
 #ifndef ULY_BAND
-#define ULY_BAND 256
+#define ULY_BAND 0
 #endif
 
-// Launch table of one relayout pass: row bands of about ULY_BAND vectors
-// when ULY_BAND > 0, else flat blocks in kRelayoutOrder.
+// Launch table of one relayout pass: bands of ULY_VBAND vectors when
+// ULY_VBAND > 0, else row bands of about ULY_BAND vectors when ULY_BAND > 0,
+// else flat blocks in kRelayoutOrder.
+#ifndef ULY_VBAND
+#define ULY_VBAND 256
+#endif
+
 static uint32_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
+    if (ULY_VBAND > 0) return ulysses::fill_relayout_vbands(p, mode, ULY_VBAND, a);
     if (ULY_BAND > 0)
         return ulysses::fill_relayout_bands(p, mode, ulysses::band_rows_for(p, mode, ULY_BAND), a);
     return ulysses::fill_relayout(p, mode, ulysses::relayout_vectors_per_block(), kRelayoutOrder,
@@ -297,9 +307,13 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         rc = check_overlap(ranges);
         if (rc) return rc;
 
+        // one lane moves `vpl` consecutive vectors of a head row
+        const uint32_t vpl = ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
         ulysses::RelayoutArgs t;
-        const uint32_t gx = ulysses::fill_relayout(p, 0, ulysses::fused_vectors_per_block(),
+        const uint32_t gx = ulysses::fill_relayout(p, 0, ulysses::fused_units_per_block() * vpl,
                                                    ulysses::kSrcMajor, &t);
+        if (!ulysses::to_units(&t, vpl))
+            return set_error(ULYSSES_EINVAL, "fused launch table not divisible into lane units");
         ulysses::FusedArgs a;
         std::memset(&a, 0, sizeof a);
         for (int r = 0; r < p.world; ++r) {
@@ -317,6 +331,7 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         a.rope_cos = rope_cos;
         a.rope_sin = rope_sin;
         a.eps = eps;
+        a.inv_d = 1.0f / static_cast<float>(p.d);   // exact: d is a power of two
         a.d = static_cast<uint32_t>(p.d);
         return launch_status(ulysses::launch_fused(a, gx, static_cast<uint32_t>(p.b), stream),
                              "fused relayout");

@@ -46,8 +46,17 @@
 #ifndef ULY_NT
 #define ULY_NT 3
 #endif
+#ifndef ULY_FUSED_BLOCK
+#define ULY_FUSED_BLOCK ULY_BLOCK
+#endif
 #ifndef ULY_FUSED_UNROLL
 #define ULY_FUSED_UNROLL 2
+#endif
+// 16-byte vectors of one head row per lane in the fused kernel (1, 2 or 4).
+// One is fastest on MI355X: two or four make each load instruction of a
+// wave touch two or four times the cache lines.
+#ifndef ULY_FUSED_VPL
+#define ULY_FUSED_VPL 1
 #endif
 
 namespace ulysses {
@@ -69,13 +78,15 @@ __device__ __forceinline__ void store16(unsigned char *p, u32x4 v) {
     else *q = v;
 }
 
-// The piece owning block x: blk_begin is ascending over used entries and
-// 0xFFFFFFFF past them, so the count of entries <= x (minus the first) is
-// the index.  Uniform across the block; the scan unrolls into scalar ops.
+// The piece owning block x: the last entry of blk_begin that is <= x.
+// blk_begin is strictly ascending over used entries (blk_begin[0] == 0) and
+// 0xFFFFFFFF past them.  Six dependent scalar loads of a binary search; a
+// full 64-entry scan would hold 64 SGPRs and spill.
 __device__ __forceinline__ uint32_t find_piece(const uint32_t *blk_begin, uint32_t x) {
     uint32_t p = 0;
 #pragma unroll
-    for (int q = 1; q < kMaxPieces; ++q) p += (blk_begin[q] <= x) ? 1u : 0u;
+    for (uint32_t step = kMaxPieces / 2; step > 0; step /= 2)
+        if (blk_begin[p + step] <= x) p += step;
     return p;
 }
 
@@ -154,8 +165,9 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
     const uint32_t band = local / a.world;
     const uint32_t k = local - band * a.world;
     const PieceArgs pc = a.piece[g * a.world + k];
-    const uint32_t begin = band * a.band_rows * pc.vpr;
-    const uint32_t end = min(begin + a.band_rows * pc.vpr, pc.nvec);
+    const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * pc.vpr;
+    const uint32_t begin = band * span;
+    const uint32_t end = min(begin + span, pc.nvec);
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
     const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
@@ -192,7 +204,7 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
     if (grid_x == 0 || planes == 0) return hipSuccess;
     void *argv[] = {const_cast<RelayoutArgs *>(&a)};
     const void *fn =
-        a.band_rows != 0
+        (a.band_rows != 0 || a.band_vecs != 0)
             ? reinterpret_cast<const void *>(
                   &relayout_band_kernel<ULY_BLOCK, ULY_UNROLL, (ULY_NT & 1) != 0,
                                         (ULY_NT & 2) != 0>)
@@ -207,18 +219,21 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
 // Fused mode 0 with QK RMSNorm + RoPE (bf16 in, bf16 out, fp32 arithmetic)
 // --------------------------------------------------------------------------
 //
-// A head row of d bf16 elements is L = d/8 consecutive 16-byte vectors, so L
-// consecutive lanes hold one head row, lane l holding elements 8l..8l+7 and
-// rotary pairs 4l..4l+3.  Row boundaries fall on multiples of L in the flat
-// vector index and blocks start on multiples of L, so lane l of a thread is
-// threadIdx.x % L for every vector the thread touches.  The operation order
-// is fixed so the result is reproducible bit for bit:
-//   partial = fma chain over the lane's 8 squares, ascending;
-//   ss      = xor butterfly 1, 2, 4, ... over the L lanes, which equals the
-//             pairwise tree with adjacent pairing (fp32 + is commutative, so
-//             every lane of the group ends with the same bits);
-//   inv     = 1 / sqrt(ss / d + eps), correctly rounded division and sqrt;
-//   y       = (x * inv) * gamma;  rotation with separately rounded products.
+// A head row of d bf16 elements is d/8 16-byte vectors.  Each lane holds VPL
+// consecutive vectors of one row ("a unit": elements 8*VPL*l .. 8*VPL*l +
+// 8*VPL - 1 of lane l, rotary pairs 4*VPL*l ..), so L = d / (8*VPL)
+// consecutive lanes hold one row.  The piece table arrives in units of VPL
+// vectors; rows are whole numbers of units and blocks start on multiples of
+// L, so a thread's lane within its row is threadIdx.x % L for every unit.
+// The operation order is fixed so the result is reproducible bit for bit:
+//   partial p_m, one per vector: fma chain over its 8 squares, ascending;
+//   ss = pairwise tree over p_0 .. p_{d/8-1} with adjacent pairing: the
+//        first log2(VPL) levels inside the lane, the rest as an xor
+//        butterfly over the L lanes (every lane ends with the same bits,
+//        fp32 + being commutative);
+//   ms = ss * (1/d), which equals ss / d exactly since d is a power of two;
+//   inv = 1 / sqrt(ms + eps), correctly rounded sqrt and division;
+//   y = (x * inv) * gamma;  rotation products rounded one by one.
 // The library is compiled with -ffp-contract=off so no product is fused.
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -233,38 +248,61 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over groups of L consecutive lanes; every lane of a group gets the
+// same bits.  Within a 16-lane DPP row: neighbours (quad_perm 1,0,3,2), pairs
+// of neighbours (quad_perm 2,3,0,1), then the mirrored half-row and row;
+// after each stage all lanes of a half are equal, so the mirror adds the two
+// halves, as an xor butterfly would.  Wider groups continue with shuffles.
 template <int L>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-    for (int m = 1; m < L; m <<= 1) v = v + __shfl_xor(v, m, L);
+    if constexpr (L >= 2) v = v + dpp<0xB1>(v);    // quad_perm [1,0,3,2]
+    if constexpr (L >= 4) v = v + dpp<0x4E>(v);    // quad_perm [2,3,0,1]
+    if constexpr (L >= 8) v = v + dpp<0x141>(v);   // row_half_mirror
+    if constexpr (L >= 16) v = v + dpp<0x140>(v);  // row_mirror
+    if constexpr (L >= 32) v = v + __shfl_xor(v, 16, L);
+    if constexpr (L >= 64) v = v + __shfl_xor(v, 32, L);
     return v;
 }
 
-template <int BLOCK, int UNROLL, int L>
+template <int BLOCK, int UNROLL, int VPL, int L>
 __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
+    constexpr int E = 8 * VPL;   // elements per lane
     const uint32_t x = blockIdx.x;
     const uint32_t tensor = blockIdx.z;
     const uint32_t p = find_piece(a.blk_begin, x);
-    const PieceArgs pc = a.piece[p];
+    const PieceArgs pc = a.piece[p];   // in units of VPL vectors
     const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
     const uint32_t row0 = s0 / pc.vpr;
     const uint32_t col0 = s0 - row0 * pc.vpr;
     const uint64_t plane = blockIdx.y;
     const unsigned char *sb =
-        a.src[tensor][pc.j] + (plane * a.src_plane[pc.j] + pc.src_off) * 16;
-    unsigned char *db = a.dst[tensor][pc.r] + (plane * a.dst_plane[pc.r] + pc.dst_off) * 16;
+        a.src[tensor][pc.j] + (plane * a.src_plane[pc.j] + pc.src_off) * (16 * VPL);
+    unsigned char *db =
+        a.dst[tensor][pc.r] + (plane * a.dst_plane[pc.r] + pc.dst_off) * (16 * VPL);
     const uint32_t lane = threadIdx.x & (L - 1);
     const uint32_t half_d = a.d / 2;
 
-    // this lane's 8 gains
-    const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
-    const f32x4 g0 = gp[0], g1 = gp[1];
-    const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    // this lane's gains
+    float g[E];
+    {
+        const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + E * lane);
+#pragma unroll
+        for (int i = 0; i < E / 4; ++i) {
+            const f32x4 t = gp[i];
+            g[4 * i] = t.x; g[4 * i + 1] = t.y; g[4 * i + 2] = t.z; g[4 * i + 3] = t.w;
+        }
+    }
     const float eps = a.eps;
-    const float dflt = float(a.d);
+    const float inv_d = a.inv_d;
 
-    u32x4 xv[UNROLL];
-    f32x4 cv[UNROLL], sv[UNROLL];
+    u32x4 xv[UNROLL][VPL];
+    f32x4 cv[UNROLL][VPL], sv[UNROLL][VPL];
     uint64_t doff[UNROLL];
     bool ok[UNROLL];
 #pragma unroll
@@ -278,73 +316,117 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
         const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
         doff[k] = uint64_t(row) * pc.dst_pitch + col;
         // global sequence position of this source row
-        const uint64_t tab = uint64_t(pc.src_row0 + row) * half_d + 4 * lane;
-        xv[k] = u32x4{0, 0, 0, 0};
-        cv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-        sv[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint64_t tab = uint64_t(pc.src_row0 + row) * half_d + 4 * VPL * lane;
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            xv[k][v] = u32x4{0, 0, 0, 0};
+            cv[k][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+            sv[k][v] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         if (ok[k]) {
-            xv[k] = load16<true>(sb + soff * 16);
-            cv[k] = *reinterpret_cast<const f32x4 *>(a.rope_cos + tab);
-            sv[k] = *reinterpret_cast<const f32x4 *>(a.rope_sin + tab);
+#pragma unroll
+            for (int v = 0; v < VPL; ++v) {
+                xv[k][v] = load16<true>(sb + soff * (16 * VPL) + 16 * v);
+                cv[k][v] = *reinterpret_cast<const f32x4 *>(a.rope_cos + tab + 4 * v);
+                sv[k][v] = *reinterpret_cast<const f32x4 *>(a.rope_sin + tab + 4 * v);
+            }
         }
     }
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {
-        float xf[8];
-        xf[0] = bf16_lo(xv[k].x); xf[1] = bf16_hi(xv[k].x);
-        xf[2] = bf16_lo(xv[k].y); xf[3] = bf16_hi(xv[k].y);
-        xf[4] = bf16_lo(xv[k].z); xf[5] = bf16_hi(xv[k].z);
-        xf[6] = bf16_lo(xv[k].w); xf[7] = bf16_hi(xv[k].w);
-        float part = 0.0f;
+        float xf[E];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) part = __builtin_fmaf(xf[i], xf[i], part);
-        const float ss = group_sum<L>(part);
-        // Plain '/' and __builtin_sqrtf: with hipcc's default of correctly
-        // rounded fp32 divide and sqrt these lower to the IEEE-exact
-        // sequences (div_scale/div_fmas/div_fixup; v_sqrt_f32 plus a one-ulp
-        // residual correction).  __fsqrt_rn would carry a 3-ulp fpmath bound.
-        const float ms = ss / dflt;
-        const float inv = 1.0f / __builtin_sqrtf(ms + eps);
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = (xf[i] * inv) * g[i];
-        const float c[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
-        const float s[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
-        uint32_t o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float e0 = y[2 * q] * c[q];
-            const float e1 = y[2 * q + 1] * s[q];
-            const float e2 = y[2 * q] * s[q];
-            const float e3 = y[2 * q + 1] * c[q];
-            o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+        for (int v = 0; v < VPL; ++v) {
+            xf[8 * v + 0] = bf16_lo(xv[k][v].x); xf[8 * v + 1] = bf16_hi(xv[k][v].x);
+            xf[8 * v + 2] = bf16_lo(xv[k][v].y); xf[8 * v + 3] = bf16_hi(xv[k][v].y);
+            xf[8 * v + 4] = bf16_lo(xv[k][v].z); xf[8 * v + 5] = bf16_hi(xv[k][v].z);
+            xf[8 * v + 6] = bf16_lo(xv[k][v].w); xf[8 * v + 7] = bf16_hi(xv[k][v].w);
         }
-        if (ok[k]) store16<true>(db + doff[k] * 16, u32x4{o[0], o[1], o[2], o[3]});
+        float part[VPL];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            part[v] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                part[v] = __builtin_fmaf(xf[8 * v + i], xf[8 * v + i], part[v]);
+        }
+        // adjacent-pairing levels inside the lane
+#pragma unroll
+        for (int n = VPL; n > 1; n /= 2)
+#pragma unroll
+            for (int q = 0; q < n / 2; ++q) part[q] = part[2 * q] + part[2 * q + 1];
+        const float ss = group_sum<L>(part[0]);
+        // '/' and __builtin_sqrtf lower to the IEEE-exact sequences under
+        // hipcc's default correctly rounded fp32 divide and sqrt
+        // (div_scale/div_fmas/div_fixup; v_sqrt_f32 plus a one-ulp residual
+        // correction); __fsqrt_rn would carry a 3-ulp fpmath bound.
+        const float ms = ss * inv_d;
+        const float inv = 1.0f / __builtin_sqrtf(ms + eps);
+        float y[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) y[i] = (xf[i] * inv) * g[i];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) {
+            const float c[4] = {cv[k][v].x, cv[k][v].y, cv[k][v].z, cv[k][v].w};
+            const float sn[4] = {sv[k][v].x, sv[k][v].y, sv[k][v].z, sv[k][v].w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float y0 = y[8 * v + 2 * q], y1 = y[8 * v + 2 * q + 1];
+                const float e0 = y0 * c[q];
+                const float e1 = y1 * sn[q];
+                const float e2 = y0 * sn[q];
+                const float e3 = y1 * c[q];
+                o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+            }
+            if (ok[k])
+                store16<true>(db + doff[k] * (16 * VPL) + 16 * v, u32x4{o[0], o[1], o[2], o[3]});
+        }
     }
 }
 
-uint32_t fused_vectors_per_block() { return ULY_BLOCK * ULY_FUSED_UNROLL; }
+uint32_t fused_units_per_block() { return ULY_FUSED_BLOCK * ULY_FUSED_UNROLL; }
 
-template <int L>
+uint32_t fused_vectors_per_lane(uint32_t d) {
+    const uint32_t per_row = d / 8;
+    return per_row >= ULY_FUSED_VPL ? ULY_FUSED_VPL : per_row;
+}
+
+template <int VPL, int L>
 static hipError_t launch_fused_l(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
                                  hipStream_t stream) {
     void *argv[] = {const_cast<FusedArgs *>(&a)};
     return hipLaunchKernel(
-        reinterpret_cast<const void *>(&fused_kernel<ULY_BLOCK, ULY_FUSED_UNROLL, L>),
-        dim3(grid_x, planes, 2), dim3(ULY_BLOCK, 1, 1), argv, 0, stream);
+        reinterpret_cast<const void *>(&fused_kernel<ULY_FUSED_BLOCK, ULY_FUSED_UNROLL, VPL, L>),
+        dim3(grid_x, planes, 2), dim3(ULY_FUSED_BLOCK, 1, 1), argv, 0, stream);
+}
+
+template <int VPL>
+static hipError_t launch_fused_vpl(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
+                                   hipStream_t stream) {
+    switch (a.d / (8 * VPL)) {
+    case 1: return launch_fused_l<VPL, 1>(a, grid_x, planes, stream);
+    case 2: return launch_fused_l<VPL, 2>(a, grid_x, planes, stream);
+    case 4: return launch_fused_l<VPL, 4>(a, grid_x, planes, stream);
+    case 8: return launch_fused_l<VPL, 8>(a, grid_x, planes, stream);
+    case 16: return launch_fused_l<VPL, 16>(a, grid_x, planes, stream);
+    case 32: return launch_fused_l<VPL, 32>(a, grid_x, planes, stream);
+    case 64: return launch_fused_l<VPL, 64>(a, grid_x, planes, stream);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
                         hipStream_t stream) {
     if (grid_x == 0 || planes == 0) return hipSuccess;
-    switch (a.d / 8) {
-    case 1: return launch_fused_l<1>(a, grid_x, planes, stream);
-    case 2: return launch_fused_l<2>(a, grid_x, planes, stream);
-    case 4: return launch_fused_l<4>(a, grid_x, planes, stream);
-    case 8: return launch_fused_l<8>(a, grid_x, planes, stream);
-    case 16: return launch_fused_l<16>(a, grid_x, planes, stream);
-    case 32: return launch_fused_l<32>(a, grid_x, planes, stream);
-    case 64: return launch_fused_l<64>(a, grid_x, planes, stream);
+    switch (fused_vectors_per_lane(a.d)) {
+    case 1: return launch_fused_vpl<1>(a, grid_x, planes, stream);
+#if ULY_FUSED_VPL >= 2
+    case 2: return launch_fused_vpl<2>(a, grid_x, planes, stream);
+#endif
+#if ULY_FUSED_VPL >= 4
+    case 4: return launch_fused_vpl<4>(a, grid_x, planes, stream);
+#endif
     default: return hipErrorInvalidValue;
     }
 }

@@ -9,8 +9,10 @@ namespace ulysses {
 
 // 16-byte vectors one block of the relayout / copy kernels moves.
 uint32_t relayout_vectors_per_block();
-// 16-byte vectors (one per lane) one block of the fused kernel handles.
-uint32_t fused_vectors_per_block();
+// Units one block of the fused kernel handles (one unit per lane); a unit is
+// fused_vectors_per_lane(d) consecutive 16-byte vectors of one head row.
+uint32_t fused_units_per_block();
+uint32_t fused_vectors_per_lane(uint32_t d);
 
 // Relayout pass: grid (grid_x, planes).
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,

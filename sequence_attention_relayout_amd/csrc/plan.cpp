@@ -219,6 +219,55 @@ uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrd
     return static_cast<uint32_t>(blocks);
 }
 
+uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
+    clear_table(a);
+    const ModeGeom &g = p.mode[mode];
+    for (int r = 0; r < p.world; ++r) {
+        a->src_plane[r] = static_cast<uint64_t>(g.src_plane[r] / 16);
+        a->dst_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
+    }
+    a->world = static_cast<uint32_t>(p.world);
+    a->band_vecs = band_vecs;
+    uint64_t blocks = 0;
+    for (int grp = 0; grp < p.world; ++grp) {
+        uint64_t bands = 0;
+        for (int k = 0; k < p.world; ++k) {
+            const int j = mode == 0 ? grp : k;
+            const int r = mode == 0 ? k : grp;
+            PieceArgs &o = a->piece[grp * p.world + k];
+            fill_piece_args(g.piece[j * p.world + r], &o);
+            const uint64_t nb = (uint64_t(o.nvec) + band_vecs - 1) / band_vecs;
+            if (nb > bands) bands = nb;
+        }
+        a->grp_begin[grp] = static_cast<uint32_t>(blocks);
+        blocks += bands * p.world;
+    }
+    return static_cast<uint32_t>(blocks);
+}
+
+bool to_units(RelayoutArgs *a, uint32_t vpl) {
+    if (vpl == 0) return false;
+    for (int r = 0; r < kMaxWorld; ++r) {
+        if (a->src_plane[r] % vpl || a->dst_plane[r] % vpl) return false;
+        a->src_plane[r] /= vpl;
+        a->dst_plane[r] /= vpl;
+    }
+    for (int q = 0; q < kMaxPieces; ++q) {
+        PieceArgs &o = a->piece[q];
+        if (o.nvec % vpl || o.vpr % vpl || o.src_pitch % vpl || o.dst_pitch % vpl ||
+            o.src_off % vpl || o.dst_off % vpl)
+            return false;
+        o.nvec /= vpl;
+        o.vpr /= vpl;
+        o.src_pitch /= vpl;
+        o.dst_pitch /= vpl;
+        o.src_off /= vpl;
+        o.dst_off /= vpl;
+        o.magic = row_magic(o.vpr);
+    }
+    return true;
+}
+
 uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];

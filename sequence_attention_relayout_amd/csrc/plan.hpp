@@ -84,6 +84,10 @@ uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrd
 // RelayoutArgs::grp_begin): bands of `band_rows` rows.  Returns grid.x.
 uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a);
 
+// Vector-band launch table: bands of `band_vecs` vectors of each piece,
+// interleaved over the group as for row bands.  Returns grid.x.
+uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
+
 // Band height so that one band of the widest piece moves about
 // `target_vectors` 16-byte vectors (at least one row).
 uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
@@ -92,6 +96,13 @@ uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
 // each) into the destination shards: one piece per rank whose source and
 // destination rows have the same pitch.
 uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, RelayoutArgs *a);
+
+// Rescales a launch table from 16-byte vectors to units of `vpl` vectors
+// (vector counts, offsets, pitches and plane sizes divided by vpl, magic
+// multipliers recomputed); block ranges are unchanged, so the table must
+// have been filled with vec_per_block = units per block * vpl.  Returns
+// false, leaving *a unusable, if any count is not a multiple of vpl.
+bool to_units(RelayoutArgs *a, uint32_t vpl);
 
 // Magic multiplier for the kernels' division by vpr (see PieceArgs::magic).
 uint32_t row_magic(uint32_t vpr);

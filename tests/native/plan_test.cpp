@@ -48,6 +48,7 @@ struct Hit {
     int j, r;
     uint64_t src_vec, dst_vec;   // vector offsets from the shard bases
     uint32_t col;
+    uint32_t row, pos0;          // piece-local row, piece's first position
 };
 
 static bool replay(const RelayoutArgs &a, uint32_t vpb, uint32_t x, uint32_t y, uint32_t lin,
@@ -74,6 +75,8 @@ static bool replay(const RelayoutArgs &a, uint32_t vpb, uint32_t x, uint32_t y, 
     h->dst_vec = (uint64_t(a.dst_plane0) + y) * a.dst_plane[pc.r] + pc.dst_off +
                  uint64_t(row) * pc.dst_pitch + col;
     h->col = col;
+    h->row = row;
+    h->pos0 = pc.src_row0;
     return true;
 }
 
@@ -87,8 +90,9 @@ static bool replay_band(const RelayoutArgs &a, uint32_t chunk, uint32_t x, uint3
     const uint32_t band = local / a.world;
     const uint32_t k = local - band * a.world;
     const PieceArgs &pc = a.piece[g * a.world + k];
-    const uint32_t begin = band * a.band_rows * pc.vpr;
-    const uint32_t end = std::min(begin + a.band_rows * pc.vpr, pc.nvec);
+    const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * pc.vpr;
+    const uint32_t begin = band * span;
+    const uint32_t end = std::min(begin + span, pc.nvec);
     const uint32_t s0 = begin + c * chunk;
     if (s0 >= end) return false;
     const uint32_t row0 = s0 / pc.vpr;
@@ -109,6 +113,8 @@ static bool replay_band(const RelayoutArgs &a, uint32_t chunk, uint32_t x, uint3
     h->dst_vec = (uint64_t(a.dst_plane0) + y) * a.dst_plane[pc.r] + pc.dst_off +
                  uint64_t(row) * pc.dst_pitch + col;
     h->col = col;
+    h->row = row;
+    h->pos0 = pc.src_row0;
     return true;
 }
 
@@ -137,12 +143,14 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
     const int64_t hv = hb / 16;   // vectors per head row
     for (int mode = 0; mode < 2; ++mode) {
         // traversals 0, 1: flat in both piece orders; 2, 3: row bands of
-        // two heights, with chunks of vpb vectors
-        for (int trav = 0; trav < 4; ++trav) {
+        // two heights, with chunks of vpb vectors; 4: bands of vpb vectors
+        for (int trav = 0; trav < 5; ++trav) {
             RelayoutArgs a;
             uint32_t gx, nchunks = 1;
             if (trav < 2) {
                 gx = fill_relayout(p, mode, vpb, static_cast<PieceOrder>(trav), &a);
+            } else if (trav == 4) {
+                gx = fill_relayout_vbands(p, mode, vpb, &a);
             } else {
                 const uint32_t rows = trav == 2 ? band_rows_for(p, mode, vpb) : 3;
                 gx = fill_relayout_bands(p, mode, rows, &a);
@@ -225,6 +233,54 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
     }
 }
 
+// The fused kernel's tables: mode-0 pieces in units of vpl vectors.  Every
+// destination vector is covered once, from the source the definition
+// names, and a lane's position within its head row is threadIdx % (hv/vpl).
+static void check_fused_units(int world, int64_t b, int64_t d, const std::vector<int64_t> &S,
+                              const std::vector<int64_t> &H, uint32_t upb) {
+    Plan p;
+    std::string msg;
+    REQUIRE(plan_build(&p, world, b, d, S.data(), H.data(), 0, 0, &msg) == kOk, "plan");
+    const int64_t hv = d / 8, n_global = p.n_global, s_global = p.s_global;
+    for (uint32_t vpl = 1; vpl <= 4; vpl *= 2) {
+        if (hv % vpl) continue;
+        const uint32_t L = static_cast<uint32_t>(hv / vpl);
+        RelayoutArgs a;
+        const uint32_t gx = fill_relayout(p, 0, upb * vpl, kSrcMajor, &a);
+        REQUIRE(to_units(&a, vpl), "to_units");
+        std::vector<std::vector<int>> hits(world);
+        for (int r = 0; r < world; ++r)
+            hits[r].assign(static_cast<size_t>(b * p.mode[0].dst_plane[r] / 16), 0);
+        for (uint32_t y = 0; y < b; ++y)
+            for (uint32_t x = 0; x < gx; ++x)
+                for (uint32_t lin = 0; lin < upb; ++lin) {
+                    Hit h;
+                    if (!replay(a, upb, x, y, lin, &h)) continue;
+                    REQUIRE(h.col % L == lin % L, "fused lane mapping");
+                    for (uint32_t v = 0; v < vpl; ++v) {
+                        int64_t dv = static_cast<int64_t>(h.dst_vec * vpl + v);
+                        const int64_t sv = static_cast<int64_t>(h.src_vec * vpl + v);
+                        REQUIRE(dv < static_cast<int64_t>(hits[h.r].size()), "unit past shard");
+                        hits[h.r][dv] += 1;
+                        const int64_t e = dv % hv; dv /= hv;
+                        const int64_t hh = dv % p.H[h.r]; dv /= p.H[h.r];
+                        const int64_t Sg = dv % s_global, bi = dv / s_global;
+                        int j = 0;
+                        while (!(p.seq_off[j] <= Sg && Sg < p.seq_off[j + 1])) ++j;
+                        const int64_t want = ((bi * p.S[j] + (Sg - p.seq_off[j])) * n_global +
+                                              p.head_off[h.r] + hh) * hv + e;
+                        REQUIRE(h.j == j && sv == want, "fused unit source");
+                        // the table row the kernel reads is the global position
+                        REQUIRE(int64_t(h.pos0) + int64_t(h.row) == Sg, "fused rotary position");
+                    }
+                }
+        for (int r = 0; r < world; ++r)
+            for (size_t i = 0; i < hits[r].size(); ++i)
+                REQUIRE(hits[r][i] == 1, "fused coverage vpl=%u rank %d vec %zu: %d", vpl, r, i,
+                        hits[r][i]);
+    }
+}
+
 static void check_errors() {
     Plan p;
     std::string m;
@@ -277,6 +333,19 @@ int main() {
     // long rows: row length near the 32768-vector limit, vpr == 1 rows
     check_geometry(2, 1, 2048, 2, {3, 2}, {40, 24}, 2048);
     check_geometry(3, 2, 16, 5, {5, 1, 7}, {1, 1, 1}, 64);
+    for (int it = 0; it < 40; ++it) {
+        const int world = 1 + static_cast<int>(rng() % 8);
+        const int64_t d = int64_t{8} << (rng() % 6);   // 8 .. 256
+        const int64_t b = 1 + static_cast<int64_t>(rng() % 2);
+        std::vector<int64_t> S(world), H(world);
+        for (int r = 0; r < world; ++r) {
+            S[r] = static_cast<int64_t>(rng() % 30);
+            H[r] = static_cast<int64_t>(rng() % 4);
+        }
+        S[0] += 1;
+        H[world - 1] += 1;
+        check_fused_units(world, b, d, S, H, 128);
+    }
     std::printf("OK %ld\n", g_checks);
     return 0;
 }
