@@ -22,7 +22,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   cpu_baseline  the CPU oracle (single thread) on a bounded sample;
   rows       the other hot-path rows timed after the step: uneven W=7 in
              four dtypes, the plane-at-a-time QKV pack, the fused QK-norm +
-             RoPE scatter; plus a same-run device-to-device copy ceiling.
+             RoPE scatter; plus a same-run device-to-device copy (torch) and
+             this GPU's read / write / copy ceilings for the relayout's access
+             shape (probe/hbm_probe, run as a child process first).
 """
 import argparse
 import hashlib
@@ -105,6 +107,28 @@ def cpu_baseline(reps=3, budget_s=30.0):
             "seconds": round(sum(times), 2)}
 
 
+def hbm_ceilings():
+    """Runs the HBM-ceiling probe (built next to the library) as a child
+    process; returns {"copy": GB/s, "read": GB/s, "write": GB/s} or None."""
+    import subprocess
+    exe = os.path.join(ROOT, "sequence_attention_relayout_amd", "probe", "hbm_probe")
+    if not os.path.exists(exe):
+        log("hbm probe not built; skipping the ceilings")
+        return None
+    try:
+        out = subprocess.run([exe], capture_output=True, text=True, timeout=120).stdout
+    except subprocess.TimeoutExpired:
+        log("hbm probe timed out")
+        return None
+    res = {}
+    for line in out.splitlines():
+        if line.startswith("{"):
+            rec = json.loads(line)
+            if "kernel" in rec:
+                res[rec["kernel"]] = rec["gbs"]
+    return res or None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +136,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time the step only")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the HBM read/write/copy ceiling probe")
     args = ap.parse_args()
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world_env != 1:
@@ -119,6 +145,10 @@ def main():
               "GPU's HBM, and this build has no multi-GPU path. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    # the ceiling probe runs first, in a child process, before this process
+    # touches the GPU
+    ceilings = None if args.no_ceilings else hbm_ceilings()
 
     import torch
     sys.path.insert(0, ROOT)
@@ -218,6 +248,10 @@ def main():
                      "launches_timed": 2 * K},
         "d2d_copy_ceiling_gbs": round(d2d, 1),
     }
+    if ceilings:
+        result["hbm_ceilings_gbs"] = ceilings
+        if "copy" in ceilings:
+            result["relayout_over_copy_ceiling"] = round(value / ceilings["copy"], 4)
     del x0, y0, y1, x1
     torch.cuda.empty_cache()
 

@@ -52,6 +52,19 @@ def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
     return out
 
 
+PROBE = os.path.join(PKG, "probe", "hbm_probe")
+
+
+def build_probe(verbose=False):
+    """The benchmark's HBM-ceiling probe (probe/hbm_probe.hip), a standalone
+    gfx950 executable; not part of the library."""
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    _run([hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+          "-Xclang", "-packed-fp32-ops", os.path.join(PKG, "probe", "hbm_probe.hip"), "-o",
+          PROBE], verbose)
+    return PROBE
+
+
 def build_plan_test(verbose=False, build_dir=BUILD):
     """Host-only test driver of the plan (no HIP): tests/native/plan_test.cpp."""
     os.makedirs(build_dir, exist_ok=True)
