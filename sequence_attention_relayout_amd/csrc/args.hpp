@@ -75,6 +75,10 @@ struct FusedArgs {
     float eps;
     float inv_d;                     // 1/d, exact (d is a power of two)
     uint32_t d;                      // head dimension
+    // band traversal as in RelayoutArgs (band_vecs != 0), else blk_begin
+    uint32_t grp_begin[kMaxWorld];
+    uint32_t world;
+    uint32_t band_vecs;
 };
 
 }  // namespace ulysses

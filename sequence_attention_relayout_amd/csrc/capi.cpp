@@ -39,6 +39,13 @@ static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrde
 #define ULY_VBAND 256
 #endif
 
+// The fused kernel walks bands of one block each when set, else flat blocks
+// in source-major piece order.
+#ifndef ULY_FUSED_BANDS
+#define ULY_FUSED_BANDS 1
+#endif
+static const bool kFusedBands = ULY_FUSED_BANDS != 0;
+
 static uint32_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
     if (ULY_VBAND > 0) return ulysses::fill_relayout_vbands(p, mode, ULY_VBAND, a);
     if (ULY_BAND > 0)
@@ -309,9 +316,11 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
 
         // one lane moves `vpl` consecutive vectors of a head row
         const uint32_t vpl = ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
+        const uint32_t upb = ulysses::fused_units_per_block();
         ulysses::RelayoutArgs t;
-        const uint32_t gx = ulysses::fill_relayout(p, 0, ulysses::fused_units_per_block() * vpl,
-                                                   ulysses::kSrcMajor, &t);
+        const uint32_t gx =
+            kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
+                        : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
         if (!ulysses::to_units(&t, vpl))
             return set_error(ULYSSES_EINVAL, "fused launch table not divisible into lane units");
         ulysses::FusedArgs a;
@@ -326,6 +335,9 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         }
         std::memcpy(a.blk_begin, t.blk_begin, sizeof a.blk_begin);
         std::memcpy(a.piece, t.piece, sizeof a.piece);
+        std::memcpy(a.grp_begin, t.grp_begin, sizeof a.grp_begin);
+        a.world = t.world;
+        a.band_vecs = t.band_vecs;
         a.gamma[0] = gamma_q;
         a.gamma[1] = gamma_k;
         a.rope_cos = rope_cos;

@@ -58,6 +58,10 @@
 #ifndef ULY_FUSED_VPL
 #define ULY_FUSED_VPL 1
 #endif
+// Share one divide/sqrt sequence between the unroll slots of a 16-lane row.
+#ifndef ULY_FUSED_SHARE_INV
+#define ULY_FUSED_SHARE_INV 1
+#endif
 
 namespace ulysses {
 
@@ -275,9 +279,26 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
     constexpr int E = 8 * VPL;   // elements per lane
     const uint32_t x = blockIdx.x;
     const uint32_t tensor = blockIdx.z;
-    const uint32_t p = find_piece(a.blk_begin, x);
-    const PieceArgs pc = a.piece[p];   // in units of VPL vectors
-    const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
+    // the block's piece (in units of VPL vectors) and first unit: a band of
+    // the piece when the table is banded, else a flat block of it
+    PieceArgs pc;
+    uint32_t s0, end;
+    if (a.band_vecs != 0) {
+        uint32_t g = 0;
+#pragma unroll
+        for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
+        const uint32_t local = x - a.grp_begin[g];
+        const uint32_t band = local / a.world;
+        pc = a.piece[g * a.world + (local - band * a.world)];
+        s0 = band * a.band_vecs;
+        end = min(s0 + a.band_vecs, pc.nvec);
+        if (s0 >= end) return;   // uniform: the whole block is past its piece
+    } else {
+        const uint32_t p = find_piece(a.blk_begin, x);
+        pc = a.piece[p];
+        s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
+        end = pc.nvec;
+    }
     const uint32_t row0 = s0 / pc.vpr;
     const uint32_t col0 = s0 - row0 * pc.vpr;
     const uint64_t plane = blockIdx.y;
@@ -312,7 +333,7 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
         const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
         const uint32_t col = t - dr * pc.vpr;
         const uint32_t row = row0 + dr;
-        ok[k] = s0 + lin < pc.nvec;
+        ok[k] = s0 + lin < end;
         const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
         doff[k] = uint64_t(row) * pc.dst_pitch + col;
         // global sequence position of this source row
@@ -332,9 +353,12 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
             }
         }
     }
+    // Squares and row sums of every slot first, then 1/sqrt once per row.
+    float xs[UNROLL][E];
+    float ss[UNROLL];
 #pragma unroll
     for (int k = 0; k < UNROLL; ++k) {
-        float xf[E];
+        float *xf = xs[k];
 #pragma unroll
         for (int v = 0; v < VPL; ++v) {
             xf[8 * v + 0] = bf16_lo(xv[k][v].x); xf[8 * v + 1] = bf16_hi(xv[k][v].x);
@@ -355,13 +379,38 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
         for (int n = VPL; n > 1; n /= 2)
 #pragma unroll
             for (int q = 0; q < n / 2; ++q) part[q] = part[2 * q] + part[2 * q + 1];
-        const float ss = group_sum<L>(part[0]);
-        // '/' and __builtin_sqrtf lower to the IEEE-exact sequences under
-        // hipcc's default correctly rounded fp32 divide and sqrt
-        // (div_scale/div_fmas/div_fixup; v_sqrt_f32 plus a one-ulp residual
-        // correction); __fsqrt_rn would carry a 3-ulp fpmath bound.
-        const float ms = ss * inv_d;
-        const float inv = 1.0f / __builtin_sqrtf(ms + eps);
+        ss[k] = group_sum<L>(part[0]);
+    }
+    // '/' and __builtin_sqrtf lower to the IEEE-exact sequences under hipcc's
+    // default correctly rounded fp32 divide and sqrt (div_scale/div_fmas/
+    // div_fixup; v_sqrt_f32 plus a one-ulp residual correction); __fsqrt_rn
+    // would carry a 3-ulp fpmath bound.  ms = ss * (1/d) equals ss / d
+    // exactly because d is a power of two.
+    float invs[UNROLL];
+    if constexpr (L == 16 && (UNROLL == 2 || UNROLL == 4) && ULY_FUSED_SHARE_INV) {
+        // Every lane of a 16-lane row holds the same ss of each slot: lane k
+        // of the row computes slot k's 1/sqrt and DPP row_newbcast:k hands it
+        // back to the whole row (the same operations on the same value, so
+        // the same bits), one divide/sqrt sequence for UNROLL slots.
+        const uint32_t q = threadIdx.x & (UNROLL - 1);
+        float sel = ss[0];
+#pragma unroll
+        for (int k = 1; k < UNROLL; ++k) sel = (q == uint32_t(k)) ? ss[k] : sel;
+        const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
+        invs[0] = dpp<0x150>(mine);
+        if constexpr (UNROLL >= 2) invs[1] = dpp<0x151>(mine);
+        if constexpr (UNROLL >= 4) {
+            invs[2] = dpp<0x152>(mine);
+            invs[3] = dpp<0x153>(mine);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < UNROLL; ++k) invs[k] = 1.0f / __builtin_sqrtf(ss[k] * inv_d + eps);
+    }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+        const float *xf = xs[k];
+        const float inv = invs[k];
         float y[E];
 #pragma unroll
         for (int i = 0; i < E; ++i) y[i] = (xf[i] * inv) * g[i];

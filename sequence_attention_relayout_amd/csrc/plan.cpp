@@ -246,7 +246,8 @@ uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
 }
 
 bool to_units(RelayoutArgs *a, uint32_t vpl) {
-    if (vpl == 0) return false;
+    if (vpl == 0 || a->band_vecs % vpl) return false;
+    a->band_vecs /= vpl;
     for (int r = 0; r < kMaxWorld; ++r) {
         if (a->src_plane[r] % vpl || a->dst_plane[r] % vpl) return false;
         a->src_plane[r] /= vpl;

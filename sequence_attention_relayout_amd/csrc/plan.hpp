@@ -98,9 +98,10 @@ uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
 uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, RelayoutArgs *a);
 
 // Rescales a launch table from 16-byte vectors to units of `vpl` vectors
-// (vector counts, offsets, pitches and plane sizes divided by vpl, magic
-// multipliers recomputed); block ranges are unchanged, so the table must
-// have been filled with vec_per_block = units per block * vpl.  Returns
+// (vector counts, offsets, pitches, plane sizes and band width divided by
+// vpl, magic multipliers recomputed); block ranges are unchanged, so the
+// table must have been filled with vec_per_block (or band_vecs) = units per
+// block * vpl.  Returns
 // false, leaving *a unusable, if any count is not a multiple of vpl.
 bool to_units(RelayoutArgs *a, uint32_t vpl);
 

@@ -245,8 +245,10 @@ static void check_fused_units(int world, int64_t b, int64_t d, const std::vector
     for (uint32_t vpl = 1; vpl <= 4; vpl *= 2) {
         if (hv % vpl) continue;
         const uint32_t L = static_cast<uint32_t>(hv / vpl);
+      for (int banded = 0; banded < 2; ++banded) {
         RelayoutArgs a;
-        const uint32_t gx = fill_relayout(p, 0, upb * vpl, kSrcMajor, &a);
+        const uint32_t gx = banded ? fill_relayout_vbands(p, 0, upb * vpl, &a)
+                                   : fill_relayout(p, 0, upb * vpl, kSrcMajor, &a);
         REQUIRE(to_units(&a, vpl), "to_units");
         std::vector<std::vector<int>> hits(world);
         for (int r = 0; r < world; ++r)
@@ -255,7 +257,9 @@ static void check_fused_units(int world, int64_t b, int64_t d, const std::vector
             for (uint32_t x = 0; x < gx; ++x)
                 for (uint32_t lin = 0; lin < upb; ++lin) {
                     Hit h;
-                    if (!replay(a, upb, x, y, lin, &h)) continue;
+                    const bool in = banded ? replay_band(a, upb, x, y, 0, lin, &h)
+                                           : replay(a, upb, x, y, lin, &h);
+                    if (!in) continue;
                     REQUIRE(h.col % L == lin % L, "fused lane mapping");
                     for (uint32_t v = 0; v < vpl; ++v) {
                         int64_t dv = static_cast<int64_t>(h.dst_vec * vpl + v);
@@ -278,6 +282,7 @@ static void check_fused_units(int world, int64_t b, int64_t d, const std::vector
             for (size_t i = 0; i < hits[r].size(); ++i)
                 REQUIRE(hits[r][i] == 1, "fused coverage vpl=%u rank %d vec %zu: %d", vpl, r, i,
                         hits[r][i]);
+      }
     }
 }
 
