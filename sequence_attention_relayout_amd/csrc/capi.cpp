@@ -25,9 +25,10 @@ struct ulysses_plan {
 static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrder>(ULY_ORDER);
 
 // Launch table choice, by measurement on MI355X (W=8, 75,600 tokens, bf16,
-// GB/s per mode-0 + mode-1 step): bands of 256 vectors interleaved over the
-// group (~6.18 TB/s) beat row bands of ~256 vectors (~6.05), the flat walk
-// (~5.86) and longer bands (512 vectors: ~5.93).
+// GB/s per mode-0 + mode-1 step): bands of 64 vectors on one-wave blocks
+// interleaved over the group (~6.35 TB/s) beat bands of 256 on 128 x 2
+// blocks (~6.15), row bands of ~256 vectors (~6.05) and the flat walk
+// (~5.86).
 #ifndef ULY_BAND
 #define ULY_BAND 0
 #endif
@@ -36,7 +37,7 @@ static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrde
 // ULY_VBAND > 0, else row bands of about ULY_BAND vectors when ULY_BAND > 0,
 // else flat blocks in kRelayoutOrder.
 #ifndef ULY_VBAND
-#define ULY_VBAND 256
+#define ULY_VBAND 64
 #endif
 
 // The fused kernel walks bands of one block each when set, else flat blocks
@@ -257,9 +258,9 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
         if (rc) return rc;
 
         ulysses::RelayoutArgs scatter, copy;
-        const uint32_t vpb = ulysses::relayout_vectors_per_block();
         const uint32_t gs = relayout_table(p, mode, &scatter);
-        const uint32_t gc = ulysses::fill_window_copy(p, mode, vpb, &copy);
+        const uint32_t gc =
+            ulysses::fill_window_copy(p, mode, ulysses::relayout_vectors_per_block(), &copy);
         for (int r = 0; r < p.world; ++r) {
             scatter.src[r] = static_cast<const unsigned char *>(src[r]);
             scatter.dst[r] = static_cast<unsigned char *>(window[r]);

@@ -22,14 +22,14 @@
 #include "kernels.hpp"
 
 // Launch shape, chosen by measurement on MI355X (W=8, 75,600 tokens, bf16):
-// 128-thread blocks moving 2 vectors per thread in row bands of about 256
-// vectors beat larger blocks, deeper unrolls, longer bands and capped
-// occupancy.
+// one-wave blocks moving one vector per thread, in bands of 64 vectors (see
+// the band table in the plan), beat every larger block, deeper unroll,
+// longer band and capped occupancy tried.
 #ifndef ULY_BLOCK
-#define ULY_BLOCK 128
+#define ULY_BLOCK 64
 #endif
 #ifndef ULY_UNROLL
-#define ULY_UNROLL 2
+#define ULY_UNROLL 1
 #endif
 #ifndef ULY_XCD
 #define ULY_XCD 0
@@ -46,8 +46,10 @@
 #ifndef ULY_NT
 #define ULY_NT 3
 #endif
+// The fused kernel keeps two rows per thread so that they share one
+// divide/sqrt sequence (128 x 2 measured best for it).
 #ifndef ULY_FUSED_BLOCK
-#define ULY_FUSED_BLOCK ULY_BLOCK
+#define ULY_FUSED_BLOCK 128
 #endif
 #ifndef ULY_FUSED_UNROLL
 #define ULY_FUSED_UNROLL 2

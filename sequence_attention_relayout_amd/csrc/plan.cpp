@@ -269,11 +269,12 @@ bool to_units(RelayoutArgs *a, uint32_t vpl) {
     return true;
 }
 
-uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, RelayoutArgs *a) {
+uint32_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];
+    a->world = 1;   // one piece per group: group r copies window r
+    a->band_vecs = band_vecs;
     uint64_t blocks = 0;
-    int n = 0;
     for (int r = 0; r < p.world; ++r) {
         // the window of r holds one destination plane of r, rows of the
         // destination's own width, packed: copy it as (rows x row) with
@@ -282,18 +283,16 @@ uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, Relay
         const int64_t rows = mode == 0 ? p.s_global : p.S[r];
         a->src_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
         a->dst_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
-        if (rows == 0 || row_bytes == 0) continue;
         Piece pc;
         pc.j = r;
         pc.r = r;
         pc.rows = rows;
         pc.row_bytes = row_bytes;
         pc.src_pitch = pc.dst_pitch = row_bytes;
-        PieceArgs &o = a->piece[n];
+        PieceArgs &o = a->piece[r];
         fill_piece_args(pc, &o);
-        a->blk_begin[n] = static_cast<uint32_t>(blocks);
-        blocks += (o.nvec + vec_per_block - 1) / vec_per_block;
-        ++n;
+        a->grp_begin[r] = static_cast<uint32_t>(blocks);
+        blocks += (uint64_t(o.nvec) + band_vecs - 1) / band_vecs;
     }
     return static_cast<uint32_t>(blocks);
 }

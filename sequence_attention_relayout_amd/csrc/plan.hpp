@@ -93,9 +93,10 @@ uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
 uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
 
 // Launch table of the plane copy from the W windows (one destination plane
-// each) into the destination shards: one piece per rank whose source and
-// destination rows have the same pitch.
-uint32_t fill_window_copy(const Plan &p, int mode, uint32_t vec_per_block, RelayoutArgs *a);
+// each) into the destination shards, for the band kernel: group r holds the
+// one piece copying window r (equal row pitches on both sides), in bands of
+// `band_vecs` vectors.
+uint32_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
 
 // Rescales a launch table from 16-byte vectors to units of `vpl` vectors
 // (vector counts, offsets, pitches, plane sizes and band width divided by

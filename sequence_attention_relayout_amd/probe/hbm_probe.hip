@@ -1,10 +1,11 @@
-// HBM ceilings of this GPU for the relayout's access shape: pure read, pure
-// write and contiguous copy kernels with the relayout kernel's launch shape
-// (128 threads, 2 x 16-byte vectors per thread, non-temporal hints), each
-// moving 1,548,288,000 bytes (one relayout launch of the W=8, 75,600-token
-// bf16 workload).  Measurement infrastructure for the benchmark: it prints
-// one JSON line per kernel (median of 20 timed runs after 3 warm-ups) and is
-// not part of the library.
+// HBM ceilings of this GPU for the relayout's access pattern: pure read,
+// pure write and contiguous copy kernels moving 16-byte vectors with
+// non-temporal hints, in three launch shapes (64 x 1, 128 x 1 and 128 x 2
+// threads x vectors per thread), each moving 1,548,288,000 bytes (one
+// relayout launch of the W=8, 75,600-token bf16 workload).  Measurement
+// infrastructure for the benchmark: it prints one JSON line per kernel and
+// shape (median of 20 timed runs after 3 warm-ups) and is not part of the
+// library.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -23,33 +24,39 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         }                                                                           \
     } while (0)
 
-// Block b moves vectors [256 b, 256 b + 256); lanes take i and i + 128.
-__global__ void __launch_bounds__(128) copy_kernel(const u32x4 *__restrict__ s,
-                                                   u32x4 *__restrict__ d, size_t n) {
-    const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (i < n) a = __builtin_nontemporal_load(s + i);
-    if (i + 128 < n) b = __builtin_nontemporal_load(s + i + 128);
-    if (i < n) __builtin_nontemporal_store(a, d + i);
-    if (i + 128 < n) __builtin_nontemporal_store(b, d + i + 128);
+// Block b moves vectors [B*U*b, B*U*(b+1)); lane t takes t, t + B, ...
+template <int B, int U>
+__global__ void __launch_bounds__(B) copy_kernel(const u32x4 *__restrict__ s,
+                                                 u32x4 *__restrict__ d, size_t n) {
+    const size_t i = size_t(blockIdx.x) * (B * U) + threadIdx.x;
+    u32x4 v[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+        if (i + k * B < n) v[k] = __builtin_nontemporal_load(s + i + k * B);
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+        if (i + k * B < n) __builtin_nontemporal_store(v[k], d + i + k * B);
 }
 
-__global__ void __launch_bounds__(128) read_kernel(const u32x4 *__restrict__ s,
-                                                   u32x4 *__restrict__ sink, size_t n) {
-    const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (i < n) a = __builtin_nontemporal_load(s + i);
-    if (i + 128 < n) b = __builtin_nontemporal_load(s + i + 128);
-    const u32x4 c = a ^ b;
+template <int B, int U>
+__global__ void __launch_bounds__(B) read_kernel(const u32x4 *__restrict__ s,
+                                                 u32x4 *__restrict__ sink, size_t n) {
+    const size_t i = size_t(blockIdx.x) * (B * U) + threadIdx.x;
+    u32x4 c = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+        if (i + k * B < n) c ^= __builtin_nontemporal_load(s + i + k * B);
     // keeps the loads alive; the buffers never hold this pattern
     if ((c.x & c.y & c.z & c.w) == 0xDEADBEEFu) sink[threadIdx.x] = c;
 }
 
-__global__ void __launch_bounds__(128) write_kernel(u32x4 *__restrict__ d, size_t n) {
-    const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+template <int B, int U>
+__global__ void __launch_bounds__(B) write_kernel(u32x4 *__restrict__ d, size_t n) {
+    const size_t i = size_t(blockIdx.x) * (B * U) + threadIdx.x;
     const u32x4 v = {static_cast<unsigned>(i), 1u, 2u, 3u};
-    if (i < n) __builtin_nontemporal_store(v, d + i);
-    if (i + 128 < n) __builtin_nontemporal_store(v, d + i + 128);
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+        if (i + k * B < n) __builtin_nontemporal_store(v, d + i + k * B);
 }
 
 int main() {
@@ -66,8 +73,7 @@ int main() {
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
-    auto blocks = [](size_t n) { return dim3(static_cast<unsigned>((n + 255) / 256)); };
-    auto run = [&](const char *name, auto launch) -> int {
+    auto run = [&](const char *kind, int blk, int u, auto launch) -> int {
         std::vector<float> t;
         for (int r = 0; r < 23; ++r) {
             CHECK(hipEventRecord(e0, 0));
@@ -81,24 +87,35 @@ int main() {
         }
         std::sort(t.begin(), t.end());
         const float med = t[t.size() / 2];
-        std::printf("{\"kernel\": \"%s\", \"bytes\": %zu, \"median_us\": %.1f, \"gbs\": %.1f}\n",
-                    name, moved, med * 1e3, moved / (med * 1e-3) / 1e9);
+        std::printf("{\"kernel\": \"%s\", \"block\": %d, \"per_thread\": %d, \"bytes\": %zu, "
+                    "\"median_us\": %.1f, \"gbs\": %.1f}\n",
+                    kind, blk, u, moved, med * 1e3, moved / (med * 1e-3) / 1e9);
         std::fflush(stdout);
         return 0;
     };
-    if (run("copy", [&] {
-            copy_kernel<<<blocks(n_copy), 128>>>(reinterpret_cast<const u32x4 *>(a),
-                                                 reinterpret_cast<u32x4 *>(b), n_copy);
-        }))
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(a);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(b);
+#define SHAPE(B, U)                                                                        \
+    if (run("copy", B, U, [&] {                                                            \
+            copy_kernel<B, U><<<dim3(unsigned((n_copy + B * U - 1) / (B * U))), B>>>(      \
+                src, dst, n_copy);                                                         \
+        }))                                                                                \
+        return 1;                                                                          \
+    if (run("read", B, U, [&] {                                                            \
+            read_kernel<B, U><<<dim3(unsigned((n_all + B * U - 1) / (B * U))), B>>>(src,   \
+                                                                                 sink,     \
+                                                                                 n_all);   \
+        }))                                                                                \
+        return 1;                                                                          \
+    if (run("write", B, U, [&] {                                                           \
+            write_kernel<B, U><<<dim3(unsigned((n_all + B * U - 1) / (B * U))), B>>>(dst,  \
+                                                                                  n_all);  \
+        }))                                                                                \
         return 1;
-    if (run("read", [&] {
-            read_kernel<<<blocks(n_all), 128>>>(reinterpret_cast<const u32x4 *>(a), sink, n_all);
-        }))
-        return 1;
-    if (run("write", [&] {
-            write_kernel<<<blocks(n_all), 128>>>(reinterpret_cast<u32x4 *>(b), n_all);
-        }))
-        return 1;
+    SHAPE(64, 1)
+    SHAPE(128, 1)
+    SHAPE(128, 2)
+#undef SHAPE
     CHECK(hipDeviceSynchronize());
     CHECK(hipFree(a));
     CHECK(hipFree(b));

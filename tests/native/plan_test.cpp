@@ -219,7 +219,7 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
             for (uint32_t x = 0; x < gc; ++x)
                 for (uint32_t lin = 0; lin < vpb; ++lin) {
                     Hit h;
-                    if (!replay(c, vpb, x, 0, lin, &h)) continue;
+                    if (!replay_band(c, vpb, x, 0, 0, lin, &h)) continue;
                     REQUIRE(h.j == h.r, "copy crosses ranks");
                     const uint64_t plane = p.mode[mode].dst_plane[h.r] / 16;
                     REQUIRE(h.dst_vec == y * plane + h.src_vec, "copy offset");
