@@ -31,9 +31,10 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
+def build(verbose=False, defines=(), out=LIB, build_dir=BUILD, kernel_src=None):
     """Compile and link; `defines` (e.g. ["ULY_UNROLL=8"]) override the
-    kernels' compile-time launch constants."""
+    kernels' compile-time launch constants; `kernel_src` replaces
+    csrc/kernels.hip (for experiments built outside the package)."""
     os.makedirs(build_dir, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     dflags = [f"-D{d}" for d in defines]
@@ -43,8 +44,8 @@ def build(verbose=False, defines=(), out=LIB, build_dir=BUILD):
         _run(["g++", *HOST_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
     kobj = os.path.join(build_dir, "kernels.o")
-    _run([hipcc, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, "kernels.hip"), "-o", kobj],
-         verbose)
+    _run([hipcc, *DEVICE_FLAGS, *dflags, f"-I{CSRC}", "-c",
+          kernel_src or os.path.join(CSRC, "kernels.hip"), "-o", kobj], verbose)
     objs.append(kobj)
     tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)

@@ -318,10 +318,12 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         // one lane moves `vpl` consecutive vectors of a head row
         const uint32_t vpl = ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
         const uint32_t upb = ulysses::fused_units_per_block();
+        const uint32_t rpb = ulysses::fused_rows_per_block(static_cast<uint32_t>(p.d));
         ulysses::RelayoutArgs t;
         const uint32_t gx =
-            kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
-                        : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
+            rpb != 0      ? ulysses::fill_relayout_bands(p, 0, rpb, &t)
+            : kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
+                          : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
         if (!ulysses::to_units(&t, vpl))
             return set_error(ULYSSES_EINVAL, "fused launch table not divisible into lane units");
         ulysses::FusedArgs a;

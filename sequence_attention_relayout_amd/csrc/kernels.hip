@@ -60,6 +60,17 @@
 #ifndef ULY_FUSED_VPL
 #define ULY_FUSED_VPL 1
 #endif
+// Row-wise fused kernel for d = 128 (one table read per destination row).
+#ifndef ULY_FUSED_ROWS
+#define ULY_FUSED_ROWS 1
+#endif
+#ifndef ULY_FUSED_ROWS_BLOCK
+#define ULY_FUSED_ROWS_BLOCK 64
+#endif
+// heads of a row handled per divide/sqrt sequence (at most 8)
+#ifndef ULY_FUSED_HC
+#define ULY_FUSED_HC 8
+#endif
 // Share one divide/sqrt sequence between the unroll slots of a 16-lane row.
 #ifndef ULY_FUSED_SHARE_INV
 #define ULY_FUSED_SHARE_INV 1
@@ -436,6 +447,118 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
     }
 }
 
+// Row-wise form for d = 128 (16 lanes per head row): a 16-lane group owns one
+// destination row of one piece and walks its heads, so the rotary table of
+// the row (cos and sin of the row's position, 16 bytes each per lane) is
+// read once for all H_r heads instead of once per head, and lane k of the
+// group computes head k's 1/sqrt(ms + eps) for up to HC heads at a time,
+// handed to the group with DPP row_newbcast:k.  Operation order and rounding
+// are those of fused_kernel.  Blocks take row bands of BLOCK/16 rows,
+// interleaved over the pieces sharing a source shard.
+template <int BLOCK, int HC>
+__global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
+    constexpr uint32_t kRowsPerBlock = BLOCK / 16;
+    const uint32_t x = blockIdx.x;
+    const uint32_t tensor = blockIdx.z;
+    uint32_t g = 0;
+#pragma unroll
+    for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
+    const uint32_t local = x - a.grp_begin[g];
+    const uint32_t band = local / a.world;
+    const PieceArgs pc = a.piece[g * a.world + (local - band * a.world)];
+    if (pc.vpr == 0) return;                     // empty piece (no heads)
+    const uint32_t rows = pc.nvec / pc.vpr;      // uniform
+    const uint32_t row0 = band * kRowsPerBlock;
+    if (row0 >= rows) return;                    // uniform: band past the piece
+    const uint32_t heads = pc.vpr / 16;
+    const uint32_t lane = threadIdx.x & 15;
+    const uint32_t row = row0 + threadIdx.x / 16;
+    const bool row_ok = row < rows;              // uniform per 16-lane group
+    const uint64_t plane = blockIdx.y;
+    const unsigned char *src =
+        a.src[tensor][pc.j] +
+        (plane * a.src_plane[pc.j] + pc.src_off + uint64_t(row) * pc.src_pitch + lane) * 16;
+    unsigned char *dst =
+        a.dst[tensor][pc.r] +
+        (plane * a.dst_plane[pc.r] + pc.dst_off + uint64_t(row) * pc.dst_pitch + lane) * 16;
+
+    // this lane's gains and the row's rotary entries (pairs 4*lane .. +3)
+    const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
+    const f32x4 g0 = gp[0], g1 = gp[1];
+    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+    if (row_ok) {
+        const uint64_t tab = uint64_t(pc.src_row0 + row) * 64 + 4 * lane;
+        cv = *reinterpret_cast<const f32x4 *>(a.rope_cos + tab);
+        sv = *reinterpret_cast<const f32x4 *>(a.rope_sin + tab);
+    }
+    const float c[4] = {cv.x, cv.y, cv.z, cv.w};
+    const float sn[4] = {sv.x, sv.y, sv.z, sv.w};
+    const float eps = a.eps;
+    const float inv_d = a.inv_d;
+
+    for (uint32_t h0 = 0; h0 < heads; h0 += HC) {
+        const uint32_t cnt = min(uint32_t(HC), heads - h0);   // uniform
+        u32x4 xv[HC];
+        float ss[HC];
+#pragma unroll
+        for (int i = 0; i < HC; ++i) {
+            xv[i] = u32x4{0, 0, 0, 0};
+            if (row_ok && uint32_t(i) < cnt) xv[i] = load16<true>(src + (h0 + i) * 256);
+        }
+#pragma unroll
+        for (int i = 0; i < HC; ++i) {
+            const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
+                                 bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
+                                 bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xf[e], xf[e], part);
+            ss[i] = group_sum<16>(part);
+        }
+        // lane k of the group takes head k; every lane of the group holds the
+        // same ss of every head, so the broadcast value is the one each lane
+        // would have computed itself.  ms = ss * (1/d) equals ss / d exactly.
+        float sel = ss[0];
+#pragma unroll
+        for (int i = 1; i < HC; ++i) sel = (lane == uint32_t(i)) ? ss[i] : sel;
+        const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
+        float invs[HC];
+        invs[0] = dpp<0x150>(mine);
+        if constexpr (HC > 1) invs[1] = dpp<0x151>(mine);
+        if constexpr (HC > 2) invs[2] = dpp<0x152>(mine);
+        if constexpr (HC > 3) invs[3] = dpp<0x153>(mine);
+        if constexpr (HC > 4) invs[4] = dpp<0x154>(mine);
+        if constexpr (HC > 5) invs[5] = dpp<0x155>(mine);
+        if constexpr (HC > 6) invs[6] = dpp<0x156>(mine);
+        if constexpr (HC > 7) invs[7] = dpp<0x157>(mine);
+#pragma unroll
+        for (int i = 0; i < HC; ++i) {
+            const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
+                                 bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
+                                 bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
+            float y[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (xf[e] * invs[i]) * gm[e];
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float e0 = y[2 * q] * c[q];
+                const float e1 = y[2 * q + 1] * sn[q];
+                const float e2 = y[2 * q] * sn[q];
+                const float e3 = y[2 * q + 1] * c[q];
+                o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+            }
+            if (row_ok && uint32_t(i) < cnt)
+                store16<true>(dst + (h0 + i) * 256, u32x4{o[0], o[1], o[2], o[3]});
+        }
+    }
+}
+
+uint32_t fused_rows_per_block(uint32_t d) {
+    return (ULY_FUSED_ROWS && d == 128) ? ULY_FUSED_ROWS_BLOCK / 16 : 0;
+}
+
 uint32_t fused_units_per_block() { return ULY_FUSED_BLOCK * ULY_FUSED_UNROLL; }
 
 uint32_t fused_vectors_per_lane(uint32_t d) {
@@ -470,6 +593,12 @@ static hipError_t launch_fused_vpl(const FusedArgs &a, uint32_t grid_x, uint32_t
 hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
                         hipStream_t stream) {
     if (grid_x == 0 || planes == 0) return hipSuccess;
+    if (fused_rows_per_block(a.d) != 0) {
+        void *argv[] = {const_cast<FusedArgs *>(&a)};
+        return hipLaunchKernel(
+            reinterpret_cast<const void *>(&fused_rows_kernel<ULY_FUSED_ROWS_BLOCK, ULY_FUSED_HC>),
+            dim3(grid_x, planes, 2), dim3(ULY_FUSED_ROWS_BLOCK, 1, 1), argv, 0, stream);
+    }
     switch (fused_vectors_per_lane(a.d)) {
     case 1: return launch_fused_vpl<1>(a, grid_x, planes, stream);
 #if ULY_FUSED_VPL >= 2

@@ -13,6 +13,9 @@ uint32_t relayout_vectors_per_block();
 // fused_vectors_per_lane(d) consecutive 16-byte vectors of one head row.
 uint32_t fused_units_per_block();
 uint32_t fused_vectors_per_lane(uint32_t d);
+// Rows per block of the row-wise fused kernel for head dimension d (it reads
+// a row-band table, fill_relayout_bands), or 0 when d takes fused_kernel.
+uint32_t fused_rows_per_block(uint32_t d);
 
 // Relayout pass: grid (grid_x, planes).
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,

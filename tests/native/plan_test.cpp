@@ -286,6 +286,60 @@ static void check_fused_units(int world, int64_t b, int64_t d, const std::vector
     }
 }
 
+// The row-wise fused kernel (d = 128): block x of a row-band table with
+// `rpb` rows per block; a 16-lane group owns one row of the piece and walks
+// its heads.  Every destination vector once, from the defined source, and
+// the rotary position is the row's global position.
+static void check_fused_rows(int world, int64_t b, const std::vector<int64_t> &S,
+                             const std::vector<int64_t> &H, uint32_t rpb) {
+    Plan p;
+    std::string msg;
+    REQUIRE(plan_build(&p, world, b, 128, S.data(), H.data(), 0, 0, &msg) == kOk, "plan");
+    const int64_t hv = 16, n_global = p.n_global, s_global = p.s_global;
+    RelayoutArgs a;
+    const uint32_t gx = fill_relayout_bands(p, 0, rpb, &a);
+    std::vector<std::vector<int>> hits(world);
+    for (int r = 0; r < world; ++r)
+        hits[r].assign(static_cast<size_t>(b * p.mode[0].dst_plane[r] / 16), 0);
+    for (uint32_t y = 0; y < b; ++y)
+        for (uint32_t x = 0; x < gx; ++x) {
+            uint32_t g = 0;
+            for (int q = 1; q < kMaxWorld; ++q) g += a.grp_begin[q] <= x ? 1u : 0u;
+            const uint32_t local = x - a.grp_begin[g];
+            const uint32_t band = local / a.world;
+            const PieceArgs &pc = a.piece[g * a.world + (local - band * a.world)];
+            if (pc.vpr == 0) continue;
+            const uint32_t rows = pc.nvec / pc.vpr, heads = pc.vpr / 16;
+            if (band * rpb >= rows) continue;
+            for (uint32_t t = 0; t < rpb * 16; ++t) {
+                const uint32_t lane = t & 15, row = band * rpb + t / 16;
+                if (row >= rows) continue;
+                for (uint32_t h = 0; h < heads; ++h) {
+                    const uint64_t sv = uint64_t(y) * a.src_plane[pc.j] + pc.src_off +
+                                        uint64_t(row) * pc.src_pitch + lane + h * 16;
+                    const uint64_t dvv = uint64_t(y) * a.dst_plane[pc.r] + pc.dst_off +
+                                         uint64_t(row) * pc.dst_pitch + lane + h * 16;
+                    REQUIRE(dvv < hits[pc.r].size(), "rows kernel past shard");
+                    hits[pc.r][dvv] += 1;
+                    int64_t dv = static_cast<int64_t>(dvv);
+                    const int64_t e = dv % hv; dv /= hv;
+                    const int64_t hh = dv % p.H[pc.r]; dv /= p.H[pc.r];
+                    const int64_t Sg = dv % s_global, bi = dv / s_global;
+                    int j = 0;
+                    while (!(p.seq_off[j] <= Sg && Sg < p.seq_off[j + 1])) ++j;
+                    const int64_t want = ((bi * p.S[j] + (Sg - p.seq_off[j])) * n_global +
+                                          p.head_off[pc.r] + hh) * hv + e;
+                    REQUIRE(pc.j == j && int64_t(sv) == want, "rows kernel source");
+                    REQUIRE(int64_t(pc.src_row0) + int64_t(row) == Sg, "rows kernel position");
+                    REQUIRE(int64_t(lane) == e, "rows kernel lane");
+                }
+            }
+        }
+    for (int r = 0; r < world; ++r)
+        for (size_t i = 0; i < hits[r].size(); ++i)
+            REQUIRE(hits[r][i] == 1, "rows kernel coverage rank %d vec %zu: %d", r, i, hits[r][i]);
+}
+
 static void check_errors() {
     Plan p;
     std::string m;
@@ -350,6 +404,17 @@ int main() {
         S[0] += 1;
         H[world - 1] += 1;
         check_fused_units(world, b, d, S, H, 128);
+    }
+    for (int it = 0; it < 30; ++it) {
+        const int world = 1 + static_cast<int>(rng() % 8);
+        std::vector<int64_t> S(world), H(world);
+        for (int r = 0; r < world; ++r) {
+            S[r] = static_cast<int64_t>(rng() % 23);
+            H[r] = static_cast<int64_t>(rng() % 19);   // up to 18 heads: several head chunks
+        }
+        S[0] += 1;
+        H[world - 1] += 1;
+        check_fused_rows(world, 1 + static_cast<int64_t>(rng() % 2), S, H, it % 2 ? 4 : 8);
     }
     std::printf("OK %ld\n", g_checks);
     return 0;

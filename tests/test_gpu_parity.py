@@ -324,6 +324,29 @@ def test_fused_medium_full_compare(d, world, seq_total):
         assert hist[2] == 0 and hist[3] == 0
 
 
+@pytest.mark.parametrize("world,heads", [(2, [12, 9]), (1, [20]), (3, [17, 0, 8])])
+def test_fused_many_heads_full_compare(world, heads):
+    """More than 8 heads per rank: the row-wise d=128 kernel walks its heads
+    in several chunks."""
+    seq = W.seeded_partition(7, 300, world) if world > 1 else [300]
+    H.say(f"case: fused many heads W={world} seq={seq} head={heads}")
+    plan = U.ulysses_plan_create(world, 2, 128, seq, heads, "bf16")
+    wl = W.Workload("fused heads", world, 2, 128, seq, heads)
+    qs = W.make_shards(wl, 0, "bf16", 64, DEV)
+    ks = W.make_shards(wl, 0, "bf16", 65, DEV)
+    gq, gk = W.make_gamma(128, 66, DEV), W.make_gamma(128, 67, DEV)
+    tab, (oc, osn) = rope_tables(sum(seq), 128)
+    qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
+    for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
+        want = oracle.qknorm_rope_mode0(2, 128, seq, heads, [H.to_np(x) for x in src],
+                                        g.cpu().numpy(), EPS, oc, osn)
+        hist = np.zeros(4, np.int64)
+        for o, w in zip(out, want):
+            hist += ulp_hist(H.to_np(o), w)
+        H.say(f"  ulp histogram (0,1,2,>=3): {hist.tolist()}")
+        assert hist[2] == 0 and hist[3] == 0
+
+
 def test_w8_fused_full_size():
     wl = W.workloads()["w8_fused_qknorm_rope"]
     H.say(f"case: {wl.name} (sampled rows)")
