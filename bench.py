@@ -65,8 +65,11 @@ def traffic_from_profile():
     return c.get("traffic_bytes_per_launch")
 
 
-def timed(fn, reps, stream, torch):
-    """Median and min milliseconds of fn() over reps, HIP events on `stream`."""
+def timed(fn, reps, stream, torch, warmup=2):
+    """Median and min milliseconds of fn() over reps (after `warmup` untimed
+    calls), HIP events on `stream`."""
+    for _ in range(warmup):
+        fn()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for a, b in evs:
@@ -285,6 +288,43 @@ def time_rows(U, W, torch, dev, stream, reps=10):
             del xs, ys
         torch.cuda.empty_cache()
     log("uneven rows done")
+
+    # q, k and v of the timed geometry: one launch against three
+    wl = wls["w8_wan720p"]
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
+    xs = [W.make_shards(wl, 0, "bf16", 130 + t, dev) for t in range(3)]
+    ys = [[torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16,
+                       device=dev) for r in range(wl.world)] for _ in range(3)]
+    nb = 3 * U.ulysses_plan_bytes(plan, 0)
+    med_multi, _ = timed(lambda: U.ulysses_a2a_4d_multi(plan, 0, xs, ys, h), reps, stream, torch)
+
+    def three():
+        for t in range(3):
+            U.ulysses_a2a_4d(plan, 0, xs[t], ys[t], h)
+
+    med_three, _ = timed(three, reps, stream, torch)
+    rows["w8_qkv_mode0_one_launch"] = {"gbs": round(nb / (med_multi * 1e-3) / 1e9, 1),
+                                       "median_us": round(med_multi * 1e3, 1), "bytes": nb}
+    rows["w8_qkv_mode0_three_launches"] = {"gbs": round(nb / (med_three * 1e-3) / 1e9, 1),
+                                           "median_us": round(med_three * 1e3, 1)}
+    # autograd: forward (mode 0) and backward (mode 1, same plan) of one tensor
+    from sequence_attention_relayout_amd.autograd import all_to_all_4d
+    xg = [x.detach().requires_grad_() for x in xs[0]]
+    gy = [torch.ones_like(y) for y in ys[0]]
+
+    def fwd_bwd():
+        for x in xg:
+            x.grad = None   # no accumulation pass: each backward writes fresh grads
+        outs = all_to_all_4d(plan, xg, 0)
+        torch.autograd.backward(outs, gy)
+
+    med_ag, _ = timed(fwd_bwd, reps, stream, torch)
+    rows["w8_autograd_fwd_bwd"] = {
+        "gbs": round(2 * U.ulysses_plan_bytes(plan, 0) / (med_ag * 1e-3) / 1e9, 1),
+        "median_us": round(med_ag * 1e3, 1)}
+    del xs, ys, xg, gy
+    torch.cuda.empty_cache()
+    log("multi-tensor rows done")
 
     wl = wls["w4_qkv_chunked"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16",

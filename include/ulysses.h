@@ -146,6 +146,23 @@ int ulysses_a2a_4d(const ulysses_plan *plan, int mode, const void *const *src,
                    void *const *dst, hipStream_t stream);
 
 /*
+ * The relayout of several tensors of the plan's geometry in one launch, e.g.
+ * a layer's q, k and v, or a packed QKVG (fast-ulysses 0.1.0 "What it does":
+ * q/k/v calls sharing one closing handshake; FastVideo "Ulysses performance
+ * on GB200": packed QKV or QKVG).  Equal to ntensors ulysses_a2a_4d calls.
+ *
+ *   ntensors  1 .. ULYSSES_MAX_TENSORS.
+ *   src, dst  host arrays of ntensors * W device pointers, tensor-major:
+ *             entry t * W + r is rank r's shard of tensor t.
+ *
+ * Same pointer rules as ulysses_a2a_4d, over all tensors: no destination
+ * may overlap any source or any other destination (EOVERLAP).
+ */
+#define ULYSSES_MAX_TENSORS 4
+int ulysses_a2a_4d_multi(const ulysses_plan *plan, int mode, int ntensors,
+                         const void *const *src, void *const *dst, hipStream_t stream);
+
+/*
  * Plane-at-a-time relayout under a window cap (FastVideo "Ulysses
  * performance on GB200": one batch plane is exchanged at a time; each rank
  * keeps at most 1 GiB of window; the full output still needs its own

@@ -2,7 +2,7 @@
 //
 // Plain C++ types only (no HIP headers), so the plan that fills them builds
 // and is unit-tested without a GPU.  Every block is passed to its kernel by
-// value through the kernarg segment; each stays well under 4 KiB.
+// value through the kernarg segment; each stays under 4 KiB (checked below).
 #pragma once
 #include <cstdint>
 
@@ -10,6 +10,8 @@ namespace ulysses {
 
 constexpr int kMaxWorld = 8;
 constexpr int kMaxPieces = kMaxWorld * kMaxWorld;
+// Tensors one relayout launch can move (q, k, v and a gate: QKVG).
+constexpr int kMaxTensors = 4;
 // A row of any shard is at most this many 16-byte vectors (512 KiB).  The
 // kernels split a block's vector range into rows with a 32-bit
 // multiply-high whose numerators stay below 2^16 under this bound.
@@ -33,11 +35,12 @@ struct PieceArgs {
 };
 
 // Launch table for one relayout pass: grid.x walks the pieces' blocks, grid.y
-// the batch planes.  Block x belongs to the piece p with
-// blk_begin[p] <= x < blk_begin[p + 1]; unused entries hold 0xFFFFFFFF.
+// the batch planes, grid.z the tensors (all of one plan's geometry).  Block x
+// belongs to the piece p with blk_begin[p] <= x < blk_begin[p + 1]; unused
+// entries hold 0xFFFFFFFF.
 struct RelayoutArgs {
-    const unsigned char *src[kMaxWorld];
-    unsigned char *dst[kMaxWorld];
+    const unsigned char *src[kMaxTensors][kMaxWorld];
+    unsigned char *dst[kMaxTensors][kMaxWorld];
     uint64_t src_plane[kMaxWorld];   // vectors per batch plane of source shard j
     uint64_t dst_plane[kMaxWorld];   // vectors per batch plane of destination shard r
     uint32_t blk_begin[kMaxPieces];
@@ -80,5 +83,8 @@ struct FusedArgs {
     uint32_t world;
     uint32_t band_vecs;
 };
+
+static_assert(sizeof(RelayoutArgs) <= 4096, "kernel argument block over 4 KiB");
+static_assert(sizeof(FusedArgs) <= 4096, "kernel argument block over 4 KiB");
 
 }  // namespace ulysses

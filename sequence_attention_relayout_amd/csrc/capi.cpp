@@ -141,12 +141,44 @@ int check_shards(const ulysses::Plan &p, int mode, const void *const *src, void 
     return ULYSSES_OK;
 }
 
-void set_pointers(const ulysses::Plan &p, const void *const *src, void *const *dst,
-                  ulysses::RelayoutArgs *a) {
-    for (int r = 0; r < p.world; ++r) {
-        a->src[r] = static_cast<const unsigned char *>(src[r]);
-        a->dst[r] = static_cast<unsigned char *>(dst[r]);
+// Pointers of tensor t: src/dst hold W entries per tensor, tensor-major.
+void set_pointers(const ulysses::Plan &p, int tensors, const void *const *src,
+                  void *const *dst, ulysses::RelayoutArgs *a) {
+    for (int t = 0; t < tensors; ++t)
+        for (int r = 0; r < p.world; ++r) {
+            a->src[t][r] = static_cast<const unsigned char *>(src[t * p.world + r]);
+            a->dst[t][r] = static_cast<unsigned char *>(dst[t * p.world + r]);
+        }
+}
+
+// Validation and launch shared by the one-tensor and multi-tensor calls.
+int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void *const *src,
+                     void *const *dst, hipStream_t stream);
+
+int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void *const *src,
+                     void *const *dst, hipStream_t stream) {
+    int rc = check_plan_mode(plan, mode);
+    if (rc) return rc;
+    if (tensors < 1 || tensors > ulysses::kMaxTensors)
+        return set_error(ULYSSES_EINVAL, "ntensors must be in [1, 4]");
+    if (!src || !dst) return set_error(ULYSSES_EINVAL, "pointer arrays must be non-null");
+    const ulysses::Plan &p = plan->p;
+    std::vector<Range> ranges;
+    for (int t = 0; t < tensors; ++t) {
+        const std::string sn = tensors == 1 ? "src" : "src" + std::to_string(t);
+        const std::string dn = tensors == 1 ? "dst" : "dst" + std::to_string(t);
+        rc = check_shards(p, mode, src + t * p.world, dst + t * p.world, sn.c_str(), dn.c_str(),
+                          &ranges);
+        if (rc) return rc;
     }
+    rc = check_overlap(ranges);
+    if (rc) return rc;
+    ulysses::RelayoutArgs a;
+    const uint32_t gx = relayout_table(p, mode, &a);
+    set_pointers(p, tensors, src, dst, &a);
+    return launch_status(ulysses::launch_relayout(a, gx, static_cast<uint32_t>(p.b),
+                                                  static_cast<uint32_t>(tensors), stream),
+                         "relayout");
 }
 
 }  // namespace
@@ -213,21 +245,13 @@ int64_t ulysses_plan_bytes(const ulysses_plan *plan, int mode) {
 
 int ulysses_a2a_4d(const ulysses_plan *plan, int mode, const void *const *src,
                    void *const *dst, hipStream_t stream) {
-    return guarded([&]() -> int {
-        int rc = check_plan_mode(plan, mode);
-        if (rc) return rc;
-        const ulysses::Plan &p = plan->p;
-        std::vector<Range> ranges;
-        rc = check_shards(p, mode, src, dst, "src", "dst", &ranges);
-        if (rc) return rc;
-        rc = check_overlap(ranges);
-        if (rc) return rc;
-        ulysses::RelayoutArgs a;
-        const uint32_t gx = relayout_table(p, mode, &a);
-        set_pointers(p, src, dst, &a);
-        return launch_status(
-            ulysses::launch_relayout(a, gx, static_cast<uint32_t>(p.b), stream), "relayout");
-    });
+    return guarded([&]() -> int { return relayout_tensors(plan, mode, 1, src, dst, stream); });
+}
+
+int ulysses_a2a_4d_multi(const ulysses_plan *plan, int mode, int ntensors,
+                         const void *const *src, void *const *dst, hipStream_t stream) {
+    return guarded(
+        [&]() -> int { return relayout_tensors(plan, mode, ntensors, src, dst, stream); });
 }
 
 int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const *src,
@@ -262,19 +286,20 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
         const uint32_t gc =
             ulysses::fill_window_copy(p, mode, ulysses::relayout_vectors_per_block(), &copy);
         for (int r = 0; r < p.world; ++r) {
-            scatter.src[r] = static_cast<const unsigned char *>(src[r]);
-            scatter.dst[r] = static_cast<unsigned char *>(window[r]);
-            copy.src[r] = static_cast<const unsigned char *>(window[r]);
-            copy.dst[r] = static_cast<unsigned char *>(dst[r]);
+            scatter.src[0][r] = static_cast<const unsigned char *>(src[r]);
+            scatter.dst[0][r] = static_cast<unsigned char *>(window[r]);
+            copy.src[0][r] = static_cast<const unsigned char *>(window[r]);
+            copy.dst[0][r] = static_cast<unsigned char *>(dst[r]);
         }
         for (int64_t plane = 0; plane < p.b; ++plane) {
             scatter.src_plane0 = static_cast<uint32_t>(plane);
             scatter.dst_plane0 = 0;
-            rc = launch_status(ulysses::launch_relayout(scatter, gs, 1, stream), "chunk relayout");
+            rc = launch_status(ulysses::launch_relayout(scatter, gs, 1, 1, stream),
+                               "chunk relayout");
             if (rc) return rc;
             copy.src_plane0 = 0;
             copy.dst_plane0 = static_cast<uint32_t>(plane);
-            rc = launch_status(ulysses::launch_relayout(copy, gc, 1, stream), "window copy");
+            rc = launch_status(ulysses::launch_relayout(copy, gc, 1, 1, stream), "window copy");
             if (rc) return rc;
         }
         return ULYSSES_OK;

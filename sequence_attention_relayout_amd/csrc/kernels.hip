@@ -137,8 +137,8 @@ __global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
     const PieceArgs pc = a.piece[p];
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
-    const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
-    unsigned char *db = a.dst[pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
+    const unsigned char *sb = a.src[blockIdx.z][pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
+    unsigned char *db = a.dst[blockIdx.z][pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
 
     for (int it = 0; it < ITERS; ++it) {
         const uint32_t s0 = ((x - a.blk_begin[p]) * ITERS + it) * uint32_t(BLOCK * UNROLL);
@@ -187,8 +187,8 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
     const uint32_t end = min(begin + span, pc.nvec);
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
-    const unsigned char *sb = a.src[pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
-    unsigned char *db = a.dst[pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
+    const unsigned char *sb = a.src[blockIdx.z][pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
+    unsigned char *db = a.dst[blockIdx.z][pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
 
     for (uint32_t s0 = begin; s0 < end; s0 += uint32_t(BLOCK * UNROLL)) {
         const uint32_t row0 = s0 / pc.vpr;
@@ -217,8 +217,8 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
 uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL * ULY_ITERS; }
 
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
-                           hipStream_t stream) {
-    if (grid_x == 0 || planes == 0) return hipSuccess;
+                           uint32_t tensors, hipStream_t stream) {
+    if (grid_x == 0 || planes == 0 || tensors == 0) return hipSuccess;
     void *argv[] = {const_cast<RelayoutArgs *>(&a)};
     const void *fn =
         (a.band_rows != 0 || a.band_vecs != 0)
@@ -228,8 +228,8 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
             : reinterpret_cast<const void *>(
                   &relayout_kernel<ULY_BLOCK, ULY_UNROLL, ULY_ITERS, (ULY_NT & 1) != 0,
                                    (ULY_NT & 2) != 0>);
-    return hipLaunchKernel(fn, dim3(grid_x, planes, 1), dim3(ULY_BLOCK, 1, 1), argv, ULY_LDS,
-                           stream);
+    return hipLaunchKernel(fn, dim3(grid_x, planes, tensors), dim3(ULY_BLOCK, 1, 1), argv,
+                           ULY_LDS, stream);
 }
 
 // --------------------------------------------------------------------------

@@ -17,9 +17,10 @@ uint32_t fused_vectors_per_lane(uint32_t d);
 // a row-band table, fill_relayout_bands), or 0 when d takes fused_kernel.
 uint32_t fused_rows_per_block(uint32_t d);
 
-// Relayout pass: grid (grid_x, planes).
+// Relayout pass over `tensors` tensors of one geometry: grid (grid_x,
+// planes, tensors).
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
-                           hipStream_t stream);
+                           uint32_t tensors, hipStream_t stream);
 
 // Fused QK RMSNorm + RoPE mode-0 pass over q and k: grid (grid_x, planes, 2).
 hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,

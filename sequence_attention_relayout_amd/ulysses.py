@@ -17,6 +17,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libulysses.so")
 
 ULYSSES_MAX_WORLD = 8
+ULYSSES_MAX_TENSORS = 4
 DTYPE_CODES = {"bf16": 0, "fp16": 1, "fp32": 2, "fp8_e4m3": 3, "fp8_e5m2": 4,
                "int8": 5, "uint8": 6}
 STATUS_NAMES = {0: "ULYSSES_OK", -1: "ULYSSES_EINVAL", -2: "ULYSSES_EALIGN",
@@ -55,6 +56,8 @@ def _load():
     lib.ulysses_plan_bytes.restype = _i64
     lib.ulysses_a2a_4d.argtypes = [_p, ctypes.c_int, _p, _p, _p]
     lib.ulysses_a2a_4d.restype = ctypes.c_int
+    lib.ulysses_a2a_4d_multi.argtypes = [_p, ctypes.c_int, ctypes.c_int, _p, _p, _p]
+    lib.ulysses_a2a_4d_multi.restype = ctypes.c_int
     lib.ulysses_a2a_4d_chunked.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p]
     lib.ulysses_a2a_4d_chunked.restype = ctypes.c_int
     lib.ulysses_a2a_4d_qknorm_rope.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -190,6 +193,27 @@ def ulysses_a2a_4d(plan, mode, src, dst, stream=None):
     w = plan.world
     _check(_load().ulysses_a2a_4d(plan.handle, int(mode), _ptr_array(src, w, "src"),
                                   _ptr_array(dst, w, "dst"), _stream(stream)))
+
+
+def ulysses_a2a_4d_multi(plan, mode, srcs, dsts, stream=None):
+    """srcs, dsts: one list of W shards per tensor (at most 4 tensors)."""
+    w = plan.world
+    srcs, dsts = list(srcs), list(dsts)
+    if len(srcs) != len(dsts) or not srcs:
+        raise ValueError("need the same number (>= 1) of source and destination tensors")
+    flat_s = [x for t in srcs for x in _check_len(t, w, "src")]
+    flat_d = [x for t in dsts for x in _check_len(t, w, "dst")]
+    _check(_load().ulysses_a2a_4d_multi(plan.handle, int(mode), len(srcs),
+                                        _ptr_array(flat_s, len(flat_s), "src"),
+                                        _ptr_array(flat_d, len(flat_d), "dst"),
+                                        _stream(stream)))
+
+
+def _check_len(items, world, what):
+    items = list(items)
+    if len(items) != world:
+        raise ValueError(f"{what}: need {world} shards per tensor, got {len(items)}")
+    return items
 
 
 def ulysses_a2a_4d_chunked(plan, mode, src, dst, window, stream=None):

@@ -220,6 +220,84 @@ def test_w7_uneven_full_size(dt):
 
 
 # ---------------------------------------------------------------------------
+# several tensors in one launch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ntensors,dt,world", [(3, "bf16", 8), (4, "fp8_e4m3", 5), (2, "fp32", 3),
+                                                (1, "int8", 4)])
+def test_multi_tensor_equals_oracle(ntensors, dt, world):
+    rng = np.random.default_rng(ntensors * 10 + world)
+    seq = W.seeded_partition(int(rng.integers(0, 100)), 1200, world)
+    head = [int(v) for v in rng.integers(1, 6, world)]
+    H.say(f"case: multi ntensors={ntensors} {dt} W={world} seq={seq} head={head}")
+    plan = U.ulysses_plan_create(world, 2, 128, seq, head, dt)
+    wl = W.Workload("multi", world, 2, 128, seq, head)
+    for mode in (0, 1):
+        xs = [W.make_shards(wl, mode, dt, 120 + 10 * t + mode, DEV) for t in range(ntensors)]
+        outs = [H.Guarded(dst_shapes(plan, mode), dt, DEV) for _ in range(ntensors)]
+        U.ulysses_a2a_4d_multi(plan, mode, xs, [o.views for o in outs])
+        torch.cuda.synchronize()
+        for x, o in zip(xs, outs):
+            assert o.guards_intact()
+            check_full(mode, 2, 128, seq, head, x, o.views)
+
+
+def test_w8_qkv_multi_full_size():
+    """q, k, v of the timed geometry in one launch equal three single calls."""
+    wl = W.workloads()["w8_wan720p"]
+    H.say("case: w8 75.6k q, k, v in one launch")
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
+    xs = [W.make_shards(wl, 0, "bf16", 130 + t, DEV) for t in range(3)]
+    multi = [[torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in dst_shapes(plan, 0)]
+             for _ in range(3)]
+    U.ulysses_a2a_4d_multi(plan, 0, xs, multi)
+    single = [run_relayout(plan, 0, x, "bf16").views for x in xs]
+    torch.cuda.synchronize()
+    for m, sgl in zip(multi, single):
+        for a, b_ in zip(m, sgl):
+            assert torch.equal(bits(a), bits(b_))
+    rng = np.random.default_rng(131)
+    check_sampled(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in xs[2]],
+                  multi[2], rng, n=100_000)
+
+
+# ---------------------------------------------------------------------------
+# autograd: the backward of one mode is the other mode with the same plan
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_autograd_backward_is_the_inverse_relayout(mode):
+    from sequence_attention_relayout_amd.autograd import all_to_all_4d
+    seq, head = W.seeded_partition(11, 900, 5), [3, 1, 4, 2, 2]
+    H.say(f"case: autograd mode {mode} seq={seq} head={head}")
+    plan = U.ulysses_plan_create(5, 2, 64, seq, head, "fp32")
+    wl = W.Workload("autograd", 5, 2, 64, seq, head)
+    xs = [x.requires_grad_() for x in W.make_shards(wl, mode, "fp32", 140 + mode, DEV)]
+    ys = all_to_all_4d(plan, xs, mode)
+    check_full(mode, 2, 64, seq, head, [x.detach() for x in xs], [y.detach() for y in ys])
+    ws = W.make_shards(wl, 1 - mode, "fp32", 150 + mode, DEV)   # d loss / d y
+    loss = sum((y * w).sum() for y, w in zip(ys, ws))
+    loss.backward()
+    # d loss / d x = the inverse relayout of w, element for element
+    want = oracle.a2a_4d(1 - mode, 2, 64, seq, head, [H.to_np(w) for w in ws])
+    for x, wnt in zip(xs, want):
+        assert np.array_equal(H.to_np(x.grad), wnt)
+
+
+def test_autograd_round_trip_and_bf16():
+    from sequence_attention_relayout_amd.autograd import all_to_all_4d
+    wl = W.workloads()["w2_tiny"]
+    plan = U.ulysses_plan_create(2, 1, 128, [16, 16], [4, 4], "bf16")
+    xs = [x.requires_grad_() for x in W.make_shards(wl, 0, "bf16", 160, DEV)]
+    zs = all_to_all_4d(plan, all_to_all_4d(plan, xs, 0), 1)
+    for x, z in zip(xs, zs):
+        assert torch.equal(bits(x.detach()), bits(z.detach()))
+    sum(z.float().sum() for z in zs).backward()
+    for x in xs:
+        assert torch.equal(x.grad.float(), torch.ones_like(x.grad.float()))
+
+
+# ---------------------------------------------------------------------------
 # plane-at-a-time exchange under a window cap
 # ---------------------------------------------------------------------------
 

@@ -168,6 +168,23 @@ def test_call_errors_before_launch():
            [g, BASE + (15 << 33)], g + 64, g + 128, 1e-6, t, t + (1 << 28), 0)
 
 
+def test_multi_tensor_errors_before_launch():
+    plan = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16")
+    lib = U.library()
+    import ctypes
+    srcs = [fake(2), fake(2, off=1 << 35)]
+    dsts = [fake(2, off=1 << 36), fake(2, off=3 << 35)]
+    for n in (0, 5):
+        arr = (ctypes.c_void_p * 10)(*([BASE] * 10))
+        rc = lib.ulysses_a2a_4d_multi(plan.handle, 0, n, arr, arr, None)
+        assert rc == -1 and "ntensors" in U.ulysses_last_error()
+    # a destination of tensor 1 on a source of tensor 0
+    expect(-5, U.ulysses_a2a_4d_multi, plan, 0, srcs, [dsts[0], [srcs[0][1], dsts[1][1]]], 0)
+    # two tensors writing the same destination
+    expect(-5, U.ulysses_a2a_4d_multi, plan, 1, srcs, [dsts[0], dsts[0]], 0)
+    expect(-2, U.ulysses_a2a_4d_multi, plan, 0, [srcs[0], [srcs[1][0] + 4, srcs[1][1]]], dsts, 0)
+
+
 def test_rope_table_matches_oracle_bitwise():
     for theta, s, d in [(10000.0, 75600, 128), (500000.0, 1000, 64), (10000.0, 3, 8)]:
         c, sn = U.ulysses_rope_table(theta, s, d)
