@@ -12,11 +12,15 @@
 // permute kernels).
 //
 // Work split: grid.x walks the blocks of all pieces (a piece table in the
-// kernarg segment, block ranges found with a branch-free scan), grid.y the
-// batch planes.  A block moves ULY_BLOCK * ULY_UNROLL consecutive vectors of
-// its piece; each thread issues ULY_UNROLL independent 16-byte loads before
-// its stores, ULY_BLOCK apart, so each load instruction of a wavefront
-// covers 1 KiB of contiguous memory.
+// kernarg segment), grid.y the batch planes, grid.z the tensors.  The default
+// walk is in bands: the W pieces that share one row-sharded shard (source j
+// in mode 0, destination r in mode 1) take consecutive blocks band by band,
+// one band of ULY_BLOCK * ULY_UNROLL consecutive vectors of a piece per
+// block, so neighbouring blocks sweep whole rows of that shard and W
+// contiguous streams of the head-sharded side.  Each thread issues its
+// ULY_UNROLL 16-byte loads, ULY_BLOCK apart, before its stores; each load
+// instruction of a wavefront covers 1 KiB of contiguous memory.  A flat walk
+// (each piece's blocks in turn, relayout_kernel) remains for comparison.
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
@@ -24,23 +28,12 @@
 // Launch shape, chosen by measurement on MI355X (W=8, 75,600 tokens, bf16):
 // one-wave blocks moving one vector per thread, in bands of 64 vectors (see
 // the band table in the plan), beat every larger block, deeper unroll,
-// longer band and capped occupancy tried.
+// longer band, XCD-aware block permutation and capped occupancy tried.
 #ifndef ULY_BLOCK
 #define ULY_BLOCK 64
 #endif
 #ifndef ULY_UNROLL
 #define ULY_UNROLL 1
-#endif
-#ifndef ULY_XCD
-#define ULY_XCD 0
-#endif
-// Dynamic LDS bytes requested per relayout block (unused by the kernel);
-// a non-zero value caps how many blocks share a CU.
-#ifndef ULY_LDS
-#define ULY_LDS 0
-#endif
-#ifndef ULY_ITERS
-#define ULY_ITERS 1
 #endif
 // bit 0: non-temporal loads, bit 1: non-temporal stores
 #ifndef ULY_NT
@@ -117,55 +110,38 @@ __device__ __forceinline__ uint32_t div_vpr(uint32_t t, uint32_t vpr, uint32_t m
 // Relayout (modes 0 and 1, and the window copy of the chunked mode)
 // --------------------------------------------------------------------------
 
-// Blocks are dispatched round-robin over the 8 XCDs (block x to XCD x % 8).
-// With ULY_XCD the block index is permuted so that XCD k walks the k-th
-// contiguous eighth of the blocks (a bijection for any grid size).
-__device__ __forceinline__ uint32_t xcd_block(uint32_t x, uint32_t n) {
-#if ULY_XCD
-    const uint32_t q = n / 8, r = n % 8, xcd = x % 8, local = x / 8;
-    return xcd < r ? xcd * (q + 1) + local : r * (q + 1) + (xcd - r) * q + local;
-#else
-    (void)n;
-    return x;
-#endif
-}
-
-template <int BLOCK, int UNROLL, int ITERS, bool NTL, bool NTS>
+template <int BLOCK, int UNROLL, bool NTL, bool NTS>
 __global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
-    const uint32_t x = xcd_block(blockIdx.x, gridDim.x);
+    const uint32_t x = blockIdx.x;
     const uint32_t p = find_piece(a.blk_begin, x);
     const PieceArgs pc = a.piece[p];
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
     const unsigned char *sb = a.src[blockIdx.z][pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;
     unsigned char *db = a.dst[blockIdx.z][pc.r] + (pd * a.dst_plane[pc.r] + pc.dst_off) * 16;
-
-    for (int it = 0; it < ITERS; ++it) {
-        const uint32_t s0 = ((x - a.blk_begin[p]) * ITERS + it) * uint32_t(BLOCK * UNROLL);
-        if (s0 >= pc.nvec) break;
-        // Row and column of the chunk's first vector (uniform); per-lane
-        // offsets from there stay below 2^16 (row length <= 32768 vectors).
-        const uint32_t row0 = s0 / pc.vpr;
-        const uint32_t col0 = s0 - row0 * pc.vpr;
-        u32x4 v[UNROLL];
-        uint64_t doff[UNROLL];
-        bool ok[UNROLL];
+    const uint32_t s0 = (x - a.blk_begin[p]) * uint32_t(BLOCK * UNROLL);
+    // Row and column of the block's first vector (uniform); per-lane offsets
+    // from there stay below 2^16 (row length <= 32768 vectors).
+    const uint32_t row0 = s0 / pc.vpr;
+    const uint32_t col0 = s0 - row0 * pc.vpr;
+    u32x4 v[UNROLL];
+    uint64_t doff[UNROLL];
+    bool ok[UNROLL];
 #pragma unroll
-        for (int k = 0; k < UNROLL; ++k) {
-            const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
-            const uint32_t t = col0 + lin;
-            const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
-            const uint32_t col = t - dr * pc.vpr;
-            const uint32_t row = row0 + dr;
-            ok[k] = s0 + lin < pc.nvec;
-            const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
-            doff[k] = uint64_t(row) * pc.dst_pitch + col;
-            if (ok[k]) v[k] = load16<NTL>(sb + soff * 16);
-        }
-#pragma unroll
-        for (int k = 0; k < UNROLL; ++k)
-            if (ok[k]) store16<NTS>(db + doff[k] * 16, v[k]);
+    for (int k = 0; k < UNROLL; ++k) {
+        const uint32_t lin = threadIdx.x + uint32_t(k * BLOCK);
+        const uint32_t t = col0 + lin;
+        const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);
+        const uint32_t col = t - dr * pc.vpr;
+        const uint32_t row = row0 + dr;
+        ok[k] = s0 + lin < pc.nvec;
+        const uint64_t soff = uint64_t(row) * pc.src_pitch + col;
+        doff[k] = uint64_t(row) * pc.dst_pitch + col;
+        if (ok[k]) v[k] = load16<NTL>(sb + soff * 16);
     }
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k)
+        if (ok[k]) store16<NTS>(db + doff[k] * 16, v[k]);
 }
 
 // Row-band traversal: block x moves one band of rows of one piece; the W
@@ -174,7 +150,7 @@ __global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
 // shard and W contiguous streams of the head-sharded side.
 template <int BLOCK, int UNROLL, bool NTL, bool NTS>
 __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs a) {
-    const uint32_t x = xcd_block(blockIdx.x, gridDim.x);
+    const uint32_t x = blockIdx.x;
     uint32_t g = 0;
 #pragma unroll
     for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
@@ -214,7 +190,7 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
     }
 }
 
-uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL * ULY_ITERS; }
+uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL; }
 
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
                            uint32_t tensors, hipStream_t stream) {
@@ -226,10 +202,9 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
                   &relayout_band_kernel<ULY_BLOCK, ULY_UNROLL, (ULY_NT & 1) != 0,
                                         (ULY_NT & 2) != 0>)
             : reinterpret_cast<const void *>(
-                  &relayout_kernel<ULY_BLOCK, ULY_UNROLL, ULY_ITERS, (ULY_NT & 1) != 0,
-                                   (ULY_NT & 2) != 0>);
-    return hipLaunchKernel(fn, dim3(grid_x, planes, tensors), dim3(ULY_BLOCK, 1, 1), argv,
-                           ULY_LDS, stream);
+                  &relayout_kernel<ULY_BLOCK, ULY_UNROLL, (ULY_NT & 1) != 0, (ULY_NT & 2) != 0>);
+    return hipLaunchKernel(fn, dim3(grid_x, planes, tensors), dim3(ULY_BLOCK, 1, 1), argv, 0,
+                           stream);
 }
 
 // --------------------------------------------------------------------------
@@ -459,7 +434,6 @@ template <int BLOCK, int HC>
 __global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
     constexpr uint32_t kRowsPerBlock = BLOCK / 16;
     const uint32_t x = blockIdx.x;
-    const uint32_t tensor = blockIdx.z;
     uint32_t g = 0;
 #pragma unroll
     for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
@@ -475,17 +449,13 @@ __global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
     const uint32_t row = row0 + threadIdx.x / 16;
     const bool row_ok = row < rows;              // uniform per 16-lane group
     const uint64_t plane = blockIdx.y;
-    const unsigned char *src =
-        a.src[tensor][pc.j] +
-        (plane * a.src_plane[pc.j] + pc.src_off + uint64_t(row) * pc.src_pitch + lane) * 16;
-    unsigned char *dst =
-        a.dst[tensor][pc.r] +
-        (plane * a.dst_plane[pc.r] + pc.dst_off + uint64_t(row) * pc.dst_pitch + lane) * 16;
+    const uint64_t src_vec = plane * a.src_plane[pc.j] + pc.src_off +
+                             uint64_t(row) * pc.src_pitch + lane;
+    const uint64_t dst_vec = plane * a.dst_plane[pc.r] + pc.dst_off +
+                             uint64_t(row) * pc.dst_pitch + lane;
 
-    // this lane's gains and the row's rotary entries (pairs 4*lane .. +3)
-    const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
-    const f32x4 g0 = gp[0], g1 = gp[1];
-    const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    // the row's rotary entries (pairs 4*lane .. +3), read once for every
+    // head of the row
     f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
     if (row_ok) {
         const uint64_t tab = uint64_t(pc.src_row0 + row) * 64 + 4 * lane;
@@ -497,60 +467,70 @@ __global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
     const float eps = a.eps;
     const float inv_d = a.inv_d;
 
-    for (uint32_t h0 = 0; h0 < heads; h0 += HC) {
-        const uint32_t cnt = min(uint32_t(HC), heads - h0);   // uniform
-        u32x4 xv[HC];
-        float ss[HC];
+    {
+        const uint32_t tensor = blockIdx.z;
+        const unsigned char *src = a.src[tensor][pc.j] + src_vec * 16;
+        unsigned char *dst = a.dst[tensor][pc.r] + dst_vec * 16;
+        const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
+        const f32x4 g0 = gp[0], g1 = gp[1];
+        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+
+        for (uint32_t h0 = 0; h0 < heads; h0 += HC) {
+            const uint32_t cnt = min(uint32_t(HC), heads - h0);   // uniform
+            u32x4 xv[HC];
+            float ss[HC];
 #pragma unroll
-        for (int i = 0; i < HC; ++i) {
-            xv[i] = u32x4{0, 0, 0, 0};
-            if (row_ok && uint32_t(i) < cnt) xv[i] = load16<true>(src + (h0 + i) * 256);
-        }
-#pragma unroll
-        for (int i = 0; i < HC; ++i) {
-            const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
-                                 bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
-                                 bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
-            float part = 0.0f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xf[e], xf[e], part);
-            ss[i] = group_sum<16>(part);
-        }
-        // lane k of the group takes head k; every lane of the group holds the
-        // same ss of every head, so the broadcast value is the one each lane
-        // would have computed itself.  ms = ss * (1/d) equals ss / d exactly.
-        float sel = ss[0];
-#pragma unroll
-        for (int i = 1; i < HC; ++i) sel = (lane == uint32_t(i)) ? ss[i] : sel;
-        const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
-        float invs[HC];
-        invs[0] = dpp<0x150>(mine);
-        if constexpr (HC > 1) invs[1] = dpp<0x151>(mine);
-        if constexpr (HC > 2) invs[2] = dpp<0x152>(mine);
-        if constexpr (HC > 3) invs[3] = dpp<0x153>(mine);
-        if constexpr (HC > 4) invs[4] = dpp<0x154>(mine);
-        if constexpr (HC > 5) invs[5] = dpp<0x155>(mine);
-        if constexpr (HC > 6) invs[6] = dpp<0x156>(mine);
-        if constexpr (HC > 7) invs[7] = dpp<0x157>(mine);
-#pragma unroll
-        for (int i = 0; i < HC; ++i) {
-            const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
-                                 bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
-                                 bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
-            float y[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) y[e] = (xf[e] * invs[i]) * gm[e];
-            uint32_t o[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float e0 = y[2 * q] * c[q];
-                const float e1 = y[2 * q + 1] * sn[q];
-                const float e2 = y[2 * q] * sn[q];
-                const float e3 = y[2 * q + 1] * c[q];
-                o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+            for (int i = 0; i < HC; ++i) {
+                xv[i] = u32x4{0, 0, 0, 0};
+                if (row_ok && uint32_t(i) < cnt) xv[i] = load16<true>(src + (h0 + i) * 256);
             }
-            if (row_ok && uint32_t(i) < cnt)
-                store16<true>(dst + (h0 + i) * 256, u32x4{o[0], o[1], o[2], o[3]});
+#pragma unroll
+            for (int i = 0; i < HC; ++i) {
+                const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
+                                     bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
+                                     bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
+                float part = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xf[e], xf[e], part);
+                ss[i] = group_sum<16>(part);
+            }
+            // lane k of the group takes head k; every lane of the group holds
+            // the same ss of every head, so the broadcast value is the one
+            // each lane would have computed itself.  ms = ss * (1/d) equals
+            // ss / d exactly.
+            float sel = ss[0];
+#pragma unroll
+            for (int i = 1; i < HC; ++i) sel = (lane == uint32_t(i)) ? ss[i] : sel;
+            const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
+            float invs[HC];
+            invs[0] = dpp<0x150>(mine);
+            if constexpr (HC > 1) invs[1] = dpp<0x151>(mine);
+            if constexpr (HC > 2) invs[2] = dpp<0x152>(mine);
+            if constexpr (HC > 3) invs[3] = dpp<0x153>(mine);
+            if constexpr (HC > 4) invs[4] = dpp<0x154>(mine);
+            if constexpr (HC > 5) invs[5] = dpp<0x155>(mine);
+            if constexpr (HC > 6) invs[6] = dpp<0x156>(mine);
+            if constexpr (HC > 7) invs[7] = dpp<0x157>(mine);
+#pragma unroll
+            for (int i = 0; i < HC; ++i) {
+                const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
+                                     bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
+                                     bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = (xf[e] * invs[i]) * gm[e];
+                uint32_t o[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float e0 = y[2 * q] * c[q];
+                    const float e1 = y[2 * q + 1] * sn[q];
+                    const float e2 = y[2 * q] * sn[q];
+                    const float e3 = y[2 * q + 1] * c[q];
+                    o[q] = pack_bf16x2(e0 - e1, e2 + e3);
+                }
+                if (row_ok && uint32_t(i) < cnt)
+                    store16<true>(dst + (h0 + i) * 256, u32x4{o[0], o[1], o[2], o[3]});
+            }
         }
     }
 }
@@ -596,7 +576,8 @@ hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
     if (fused_rows_per_block(a.d) != 0) {
         void *argv[] = {const_cast<FusedArgs *>(&a)};
         return hipLaunchKernel(
-            reinterpret_cast<const void *>(&fused_rows_kernel<ULY_FUSED_ROWS_BLOCK, ULY_FUSED_HC>),
+            reinterpret_cast<const void *>(
+                &fused_rows_kernel<ULY_FUSED_ROWS_BLOCK, ULY_FUSED_HC>),
             dim3(grid_x, planes, 2), dim3(ULY_FUSED_ROWS_BLOCK, 1, 1), argv, 0, stream);
     }
     switch (fused_vectors_per_lane(a.d)) {
