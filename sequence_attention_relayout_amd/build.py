@@ -66,6 +66,21 @@ def build_probe(verbose=False):
     return PROBE
 
 
+C_CHECK = os.path.join(ROOT, "tests", "native", "abi_c_check")
+
+
+def build_c_check(verbose=False):
+    """tests/native/abi_c_check.c: a plain C99 caller of the ABI, linked
+    against libulysses.so (which must be built) and the HIP runtime."""
+    exe = C_CHECK
+    _run(["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-pedantic", "-Werror",
+          "-D__HIP_PLATFORM_AMD__", f"-isystem{ROCM}/include", f"-I{os.path.join(ROOT, 'include')}",
+          os.path.join(ROOT, "tests", "native", "abi_c_check.c"), "-o", exe, f"-L{PKG}",
+          "-lulysses", f"-Wl,-rpath,{PKG}", f"-L{ROCM}/lib", "-lamdhip64",
+          f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    return exe
+
+
 def build_plan_test(verbose=False, build_dir=BUILD):
     """Host-only test driver of the plan (no HIP): tests/native/plan_test.cpp."""
     os.makedirs(build_dir, exist_ok=True)

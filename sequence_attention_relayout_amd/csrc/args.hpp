@@ -78,6 +78,7 @@ struct FusedArgs {
     float eps;
     float inv_d;                     // 1/d, exact (d is a power of two)
     uint32_t d;                      // head dimension
+    uint32_t plane0;                 // batch plane of grid.y == 0
     // band traversal as in RelayoutArgs (band_vecs != 0), else blk_begin
     uint32_t grp_begin[kMaxWorld];
     uint32_t world;

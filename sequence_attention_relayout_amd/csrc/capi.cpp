@@ -115,6 +115,29 @@ int launch_status(hipError_t e, const char *what) {
     return set_error(ULYSSES_EHIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
+// One launch covers grid_x * block threads along x; HIP bounds that by 2^32.
+int check_grid(uint32_t grid_x, uint32_t block, const char *what) {
+    if (uint64_t(grid_x) * block > 0xFFFFFFFFull)
+        return set_error(ULYSSES_EINVAL, std::string(what) +
+                                             ": one batch plane is too large for one launch");
+    return ULYSSES_OK;
+}
+
+// A relayout over `planes` batch planes, at most kMaxGridY per launch.
+int launch_planes(ulysses::RelayoutArgs a, uint32_t gx, int64_t planes, uint32_t tensors,
+                  hipStream_t stream, const char *what) {
+    const uint32_t s0 = a.src_plane0, d0 = a.dst_plane0;
+    for (int64_t p0 = 0; p0 < planes; p0 += ulysses::kMaxGridY) {
+        const int64_t n = planes - p0 < ulysses::kMaxGridY ? planes - p0 : ulysses::kMaxGridY;
+        a.src_plane0 = s0 + static_cast<uint32_t>(p0);
+        a.dst_plane0 = d0 + static_cast<uint32_t>(p0);
+        const int rc = launch_status(
+            ulysses::launch_relayout(a, gx, static_cast<uint32_t>(n), tensors, stream), what);
+        if (rc) return rc;
+    }
+    return ULYSSES_OK;
+}
+
 int check_plan_mode(const ulysses_plan *plan, int mode) {
     if (!plan) return set_error(ULYSSES_EINVAL, "plan is null");
     if (mode != 0 && mode != 1) return set_error(ULYSSES_EINVAL, "mode must be 0 or 1");
@@ -175,10 +198,10 @@ int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void
     if (rc) return rc;
     ulysses::RelayoutArgs a;
     const uint32_t gx = relayout_table(p, mode, &a);
+    rc = check_grid(gx, ulysses::relayout_block_threads(), "relayout");
+    if (rc) return rc;
     set_pointers(p, tensors, src, dst, &a);
-    return launch_status(ulysses::launch_relayout(a, gx, static_cast<uint32_t>(p.b),
-                                                  static_cast<uint32_t>(tensors), stream),
-                         "relayout");
+    return launch_planes(a, gx, p.b, static_cast<uint32_t>(tensors), stream, "relayout");
 }
 
 }  // namespace
@@ -285,6 +308,8 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
         const uint32_t gs = relayout_table(p, mode, &scatter);
         const uint32_t gc =
             ulysses::fill_window_copy(p, mode, ulysses::relayout_vectors_per_block(), &copy);
+        rc = check_grid(gs > gc ? gs : gc, ulysses::relayout_block_threads(), "chunked relayout");
+        if (rc) return rc;
         for (int r = 0; r < p.world; ++r) {
             scatter.src[0][r] = static_cast<const unsigned char *>(src[r]);
             scatter.dst[0][r] = static_cast<unsigned char *>(window[r]);
@@ -373,8 +398,16 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         a.eps = eps;
         a.inv_d = 1.0f / static_cast<float>(p.d);   // exact: d is a power of two
         a.d = static_cast<uint32_t>(p.d);
-        return launch_status(ulysses::launch_fused(a, gx, static_cast<uint32_t>(p.b), stream),
-                             "fused relayout");
+        rc = check_grid(gx, ulysses::fused_block_threads(a.d), "fused relayout");
+        if (rc) return rc;
+        for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
+            const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
+            a.plane0 = static_cast<uint32_t>(p0);
+            rc = launch_status(ulysses::launch_fused(a, gx, static_cast<uint32_t>(n), stream),
+                               "fused relayout");
+            if (rc) return rc;
+        }
+        return ULYSSES_OK;
     });
 }
 

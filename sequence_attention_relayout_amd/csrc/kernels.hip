@@ -191,6 +191,7 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
 }
 
 uint32_t relayout_vectors_per_block() { return ULY_BLOCK * ULY_UNROLL; }
+uint32_t relayout_block_threads() { return ULY_BLOCK; }
 
 hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t planes,
                            uint32_t tensors, hipStream_t stream) {
@@ -289,7 +290,7 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
     }
     const uint32_t row0 = s0 / pc.vpr;
     const uint32_t col0 = s0 - row0 * pc.vpr;
-    const uint64_t plane = blockIdx.y;
+    const uint64_t plane = uint64_t(a.plane0) + blockIdx.y;
     const unsigned char *sb =
         a.src[tensor][pc.j] + (plane * a.src_plane[pc.j] + pc.src_off) * (16 * VPL);
     unsigned char *db =
@@ -448,7 +449,7 @@ __global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
     const uint32_t lane = threadIdx.x & 15;
     const uint32_t row = row0 + threadIdx.x / 16;
     const bool row_ok = row < rows;              // uniform per 16-lane group
-    const uint64_t plane = blockIdx.y;
+    const uint64_t plane = uint64_t(a.plane0) + blockIdx.y;
     const uint64_t src_vec = plane * a.src_plane[pc.j] + pc.src_off +
                              uint64_t(row) * pc.src_pitch + lane;
     const uint64_t dst_vec = plane * a.dst_plane[pc.r] + pc.dst_off +
@@ -540,6 +541,9 @@ uint32_t fused_rows_per_block(uint32_t d) {
 }
 
 uint32_t fused_units_per_block() { return ULY_FUSED_BLOCK * ULY_FUSED_UNROLL; }
+uint32_t fused_block_threads(uint32_t d) {
+    return fused_rows_per_block(d) != 0 ? ULY_FUSED_ROWS_BLOCK : ULY_FUSED_BLOCK;
+}
 
 uint32_t fused_vectors_per_lane(uint32_t d) {
     const uint32_t per_row = d / 8;

@@ -7,6 +7,14 @@
 
 namespace ulysses {
 
+// Most blocks along grid.y (batch planes) of one launch; callers split
+// larger batches over several launches.
+constexpr uint32_t kMaxGridY = 65535;
+// Threads per block of the relayout / copy kernels and of the fused kernel
+// chosen for head dimension d (for the grid.x * block <= 2^32 bound).
+uint32_t relayout_block_threads();
+uint32_t fused_block_threads(uint32_t d);
+
 // 16-byte vectors one block of the relayout / copy kernels moves.
 uint32_t relayout_vectors_per_block();
 // Units one block of the fused kernel handles (one unit per lane); a unit is

@@ -8,6 +8,8 @@ outputs the oracle computes one by one (plus every element of the rows at
 rank boundaries) and check the round trip on the device.  Destination
 shards sit between guard bands and are pre-filled with poison.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -504,6 +506,54 @@ def test_longest_rows_and_single_vector_rows():
         for mode in (0, 1):
             xs = W.make_shards(wl, mode, dt, 100 + mode, DEV)
             check_full(mode, b, d, seq, head, xs, run_relayout(plan, mode, xs, dt).views)
+
+
+def test_more_batch_planes_than_one_launch():
+    """70,000 batch planes: more than grid.y of one launch holds, so the
+    library splits the planes over launches (relayout, plane-at-a-time,
+    both fused kernels)."""
+    b = 70_000
+    H.say(f"case: b={b} planes")
+    seq, head = [2, 1], [1, 2]
+    plan = U.ulysses_plan_create(2, b, 8, seq, head, "bf16", 1 << 20)
+    wl = W.Workload("planes", 2, b, 8, seq, head)
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, "bf16", 170 + mode, DEV)
+        check_full(mode, b, 8, seq, head, xs, run_relayout(plan, mode, xs, "bf16").views)
+    xs = W.make_shards(wl, 0, "bf16", 172, DEV)
+    out = [torch.empty(s_, dtype=torch.bfloat16, device=DEV) for s_ in dst_shapes(plan, 0)]
+    U.ulysses_a2a_4d_chunked(plan, 0, xs, out, windows(plan, 0))
+    torch.cuda.synchronize()
+    check_full(0, b, 8, seq, head, xs, out)
+    for d in (8, 128):
+        plan_f = U.ulysses_plan_create(2, b, d, seq, head, "bf16")
+        wlf = W.Workload("planes fused", 2, b, d, seq, head)
+        qs = W.make_shards(wlf, 0, "bf16", 173, DEV)
+        ks = W.make_shards(wlf, 0, "bf16", 174, DEV)
+        gq, gk = W.make_gamma(d, 175, DEV), W.make_gamma(d, 176, DEV)
+        tab, (oc, osn) = rope_tables(sum(seq), d)
+        qo, ko = run_fused(plan_f, qs, ks, gq, gk, tab)
+        for src, o, g in ((qs, qo, gq), (ks, ko, gk)):
+            want = oracle.qknorm_rope_mode0(b, d, seq, head, [H.to_np(x) for x in src],
+                                            g.cpu().numpy(), EPS, oc, osn)
+            hist = np.zeros(4, np.int64)
+            for oo, w in zip(o, want):
+                hist += ulp_hist(H.to_np(oo), w)
+            H.say(f"  d={d} ulp histogram (0,1,2,>=3): {hist.tolist()}")
+            assert hist[2] == 0 and hist[3] == 0
+
+
+def test_plain_c_caller_round_trip():
+    """A C99 program (tests/native/abi_c_check.c, built by build()) calls the
+    ABI with hipMalloc'ed shards: mode 1 after mode 0 returns its input."""
+    import subprocess
+    from sequence_attention_relayout_amd import build as ulybuild
+    H.say("case: plain C caller, W=3 uneven bf16 round trip")
+    if not os.path.exists(ulybuild.C_CHECK):
+        pytest.fail(f"{ulybuild.C_CHECK} is not built (run __graft_entry__.build())")
+    res = subprocess.run([ulybuild.C_CHECK, "gpu"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stdout + res.stderr
+    assert res.stdout.startswith("OK gpu")
 
 
 def test_fp8_bit_patterns_survive():

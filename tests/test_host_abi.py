@@ -46,6 +46,15 @@ def test_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_plain_c_caller_host_paths():
+    """include/ulysses.h compiles as strict C99 (-pedantic -Werror) and a C
+    program links and drives the host-side calls and error paths."""
+    exe = ulybuild.build_c_check()
+    res = subprocess.run([exe, "host"], capture_output=True, text=True, timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.startswith("OK")
+
+
 def test_native_plan_replay():
     exe = ulybuild.build_plan_test()
     res = subprocess.run([exe], capture_output=True, text=True, timeout=300)
