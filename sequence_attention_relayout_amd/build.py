@@ -81,11 +81,14 @@ def build_c_check(verbose=False):
     return exe
 
 
-def build_plan_test(verbose=False, build_dir=BUILD):
-    """Host-only test driver of the plan (no HIP): tests/native/plan_test.cpp."""
+def build_plan_test(verbose=False, build_dir=BUILD, sanitize=False):
+    """Host-only test driver of the plan (no HIP): tests/native/plan_test.cpp.
+    sanitize=True builds it with AddressSanitizer and UBSan (g++, host code)."""
     os.makedirs(build_dir, exist_ok=True)
-    exe = os.path.join(build_dir, "plan_test")
-    _run(["g++", "-O2", "-std=c++17", "-Wall", f"-I{CSRC}",
+    exe = os.path.join(build_dir, "plan_test_san" if sanitize else "plan_test")
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-g",
+           "-fno-omit-frame-pointer"] if sanitize else []
+    _run(["g++", "-O1" if sanitize else "-O2", "-std=c++17", "-Wall", *san, f"-I{CSRC}",
           os.path.join(ROOT, "tests", "native", "plan_test.cpp"),
           os.path.join(CSRC, "plan.cpp"), "-o", exe], verbose)
     return exe

@@ -322,6 +322,34 @@ def test_chunked_medium_full_compare():
         check_full(mode, 3, 128, seq, head, xs, out.views)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_chunked_every_dtype(seed):
+    rng = np.random.default_rng(3000 + seed)
+    dt = W.DTYPES[seed % len(W.DTYPES)]
+    esz = W.ELEM_BYTES[dt]
+    world = int(rng.integers(1, 9))
+    b = int(rng.integers(1, 4))
+    d = (16 // esz) * int(rng.choice([1, 2, 4]))
+    seq = [int(v) for v in rng.integers(0, 300, world)]
+    head = [int(v) for v in rng.integers(0, 6, world)]
+    seq[0] += 1
+    head[-1] += 1
+    wl = W.Workload("random chunked", world, b, d, seq, head)
+    probe = U.ulysses_plan_create(world, b, d, seq, head, dt)
+    cap = max(U.ulysses_plan_window_bytes(probe, 0), U.ulysses_plan_window_bytes(probe, 1))
+    cap += int(rng.integers(0, 2)) * 4096          # exactly at the cap, or just above
+    plan = U.ulysses_plan_create(world, b, d, seq, head, dt, cap)
+    H.say(f"case: random chunked seed={seed} {dt} W={world} b={b} d={d} seq={seq} "
+          f"head={head} cap={cap}")
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, dt, 3100 + 2 * seed + mode, DEV)
+        out = H.Guarded(dst_shapes(plan, mode), dt, DEV)
+        U.ulysses_a2a_4d_chunked(plan, mode, xs, out.views, windows(plan, mode))
+        torch.cuda.synchronize()
+        assert out.guards_intact()
+        check_full(mode, b, d, seq, head, xs, out.views)
+
+
 def test_w4_qkv_chunked_full_size(golden):
     wl = W.workloads()["w4_qkv_chunked"]
     H.say(f"case: {wl.name}")
@@ -419,6 +447,34 @@ def test_fused_many_heads_full_compare(world, heads):
     qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
     for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
         want = oracle.qknorm_rope_mode0(2, 128, seq, heads, [H.to_np(x) for x in src],
+                                        g.cpu().numpy(), EPS, oc, osn)
+        hist = np.zeros(4, np.int64)
+        for o, w in zip(out, want):
+            hist += ulp_hist(H.to_np(o), w)
+        H.say(f"  ulp histogram (0,1,2,>=3): {hist.tolist()}")
+        assert hist[2] == 0 and hist[3] == 0
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_random_fused(seed):
+    rng = np.random.default_rng(4000 + seed)
+    d = int(8 << int(rng.integers(0, 7)))          # 8 .. 512
+    world = int(rng.integers(1, 9))
+    b = int(rng.integers(1, 3))
+    seq = [int(v) for v in rng.integers(0, 80, world)]
+    head = [int(v) for v in rng.integers(0, 13, world)]
+    seq[-1] += 1
+    head[0] += 1
+    H.say(f"case: random fused seed={seed} d={d} W={world} b={b} seq={seq} head={head}")
+    plan = U.ulysses_plan_create(world, b, d, seq, head, "bf16")
+    wl = W.Workload("random fused", world, b, d, seq, head)
+    qs = W.make_shards(wl, 0, "bf16", 4100 + seed, DEV)
+    ks = W.make_shards(wl, 0, "bf16", 4200 + seed, DEV)
+    gq, gk = W.make_gamma(d, 4300 + seed, DEV), W.make_gamma(d, 4400 + seed, DEV)
+    tab, (oc, osn) = rope_tables(sum(seq), d)
+    qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
+    for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
+        want = oracle.qknorm_rope_mode0(b, d, seq, head, [H.to_np(x) for x in src],
                                         g.cpu().numpy(), EPS, oc, osn)
         hist = np.zeros(4, np.int64)
         for o, w in zip(out, want):

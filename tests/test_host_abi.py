@@ -46,6 +46,16 @@ def test_exports_every_declared_symbol():
     assert set(names) <= exported
 
 
+def test_native_plan_replay_under_sanitizers():
+    """The same replay built with AddressSanitizer and UBSan: no out-of-bounds
+    access, overflow or other undefined behaviour in the plan."""
+    exe = ulybuild.build_plan_test(sanitize=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1", UBSAN_OPTIONS="halt_on_error=1")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=600, env=env)
+    assert res.returncode == 0, res.stderr[-2000:]
+    assert res.stdout.startswith("OK")
+
+
 def test_plain_c_caller_host_paths():
     """include/ulysses.h compiles as strict C99 (-pedantic -Werror) and a C
     program links and drives the host-side calls and error paths."""
