@@ -249,7 +249,9 @@ def main():
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
                      "bytes_per_launch": bytes0, "avg_launch_us": round(launch_ms * 1e3, 2),
-                     "launches_timed": 2 * K},
+                     "launches_timed": 2 * K,
+                     "mode0_median_us": round(statistics.median(m0) * 1e3, 2),
+                     "mode1_median_us": round(statistics.median(m1) * 1e3, 2)},
         "d2d_copy_ceiling_gbs": round(d2d, 1),
     }
     if ceilings:

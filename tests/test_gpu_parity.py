@@ -599,6 +599,55 @@ def test_more_batch_planes_than_one_launch():
             assert hist[2] == 0 and hist[3] == 0
 
 
+def test_graph_capture_replays_match_eager():
+    """The calls only enqueue kernels (no allocation, synchronisation or
+    memset), so they can be captured in a HIP graph: capture mode 0, mode 1
+    and the fused call once, replay three times with eager work and
+    synchronisations in between, and compare every replay with the eager
+    results."""
+    H.say("case: graph capture of mode 0 + mode 1 + fused, 3 replays")
+    seq, head = [40, 25, 31], [2, 3, 1]
+    plan = U.ulysses_plan_create(3, 2, 128, seq, head, "bf16")
+    wl = W.Workload("graph", 3, 2, 128, seq, head)
+    xs = W.make_shards(wl, 0, "bf16", 180, DEV)
+    ks = W.make_shards(wl, 0, "bf16", 181, DEV)
+    gq, gk = W.make_gamma(128, 182, DEV), W.make_gamma(128, 183, DEV)
+    tab, _ = rope_tables(sum(seq), 128)
+    shp0, shp1 = dst_shapes(plan, 0), dst_shapes(plan, 1)
+    ys = [torch.empty(sh, dtype=torch.bfloat16, device=DEV) for sh in shp0]
+    zs = [torch.empty(sh, dtype=torch.bfloat16, device=DEV) for sh in shp1]
+    qo = [torch.empty(sh, dtype=torch.bfloat16, device=DEV) for sh in shp0]
+    ko = [torch.empty(sh, dtype=torch.bfloat16, device=DEV) for sh in shp0]
+
+    def work():
+        U.ulysses_a2a_4d(plan, 0, xs, ys)
+        U.ulysses_a2a_4d(plan, 1, ys, zs)
+        U.ulysses_a2a_4d_qknorm_rope(plan, xs, qo, ks, ko, gq, gk, EPS, tab[0], tab[1])
+
+    work()
+    torch.cuda.synchronize()
+    eager = [bits(t).clone() for t in ys + zs + qo + ko]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        work()                      # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for rep in range(3):
+        for t in ys + zs + qo + ko:
+            t.zero_()               # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for e, t in zip(eager, ys + zs + qo + ko):
+            assert torch.equal(e, bits(t)), f"replay {rep} differs"
+    for x, z in zip(xs, zs):
+        assert torch.equal(bits(x), bits(z))
+
+
 def test_plain_c_caller_round_trip():
     """A C99 program (tests/native/abi_c_check.c, built by build()) calls the
     ABI with hipMalloc'ed shards: mode 1 after mode 0 returns its input."""
