@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB points the wrapper at another build of oracle.c; the mutation
+# test uses it to check that the pins catch planted mistakes.
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _i64 = ctypes.c_int64
@@ -28,6 +30,8 @@ def _load():
     if _lib is not None:
         return _lib
     if not os.path.exists(_LIB_PATH):
+        if "ORACLE_LIB" in os.environ:
+            raise ImportError(f"ORACLE_LIB={_LIB_PATH} does not exist")
         from . import build as _build
         _build.build()
     lib = ctypes.CDLL(_LIB_PATH)

@@ -17,13 +17,14 @@ CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-Wall", "-Wextra"]
 
 
-def build(verbose: bool = False) -> str:
-    cmd = ["gcc", *CFLAGS, SRC, "-o", LIB + ".tmp", "-lm"]
+def build(verbose: bool = False, src: str = SRC, out: str = LIB) -> str:
+    """Compile `src` (oracle.c, or a copy of it) into the shared library `out`."""
+    cmd = ["gcc", *CFLAGS, src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
