@@ -152,5 +152,7 @@ def index_coded_shards(wl: Workload, mode: int):
     for r in range(wl.world):
         shape = wl.shard_shape(mode, r, False)
         n = int(np.prod(shape))
+        if n >= (1 << 27) or r >= 16:
+            raise ValueError("index coding holds shards below 2^27 elements and 16 ranks")
         out.append((np.arange(n, dtype=np.int64) + (r << 27)).astype(np.int32).reshape(shape))
     return out
