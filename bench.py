@@ -225,7 +225,7 @@ def main():
     achieved = (step_bytes / 2) / (launch_ms * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); mode 0 median "
         f"{statistics.median(m0) * 1e3:.1f} us, mode 1 median {statistics.median(m1) * 1e3:.1f} us;"
-        f" host wall {wall / K * 1e3:.1f} us/step")
+        f" host wall {wall / K * 1e6:.1f} us/step")
 
     # same-run device-to-device copy of one shard set's bytes: the flat-copy
     # ceiling ("of the fabric" in the pages' terms)
@@ -290,6 +290,31 @@ def time_rows(U, W, torch, dev, stream, reps=10):
             del xs, ys
         torch.cuda.empty_cache()
     log("uneven rows done")
+
+    # the two-rank example: launch-bound, so this is latency, not bandwidth
+    wl = wls["w2_tiny"]
+    plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
+    xs = W.make_shards(wl, 0, "bf16", wl.seed, dev)
+    ys = [torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16, device=dev)
+          for r in range(wl.world)]
+    zs = [torch.empty_like(x) for x in xs]
+
+    def tiny_step():
+        U.ulysses_a2a_4d(plan, 0, xs, ys, h)
+        U.ulysses_a2a_4d(plan, 1, ys, zs, h)
+
+    med_tiny, _ = timed(tiny_step, 50, stream, torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(500):
+        tiny_step()
+    torch.cuda.synchronize()
+    host_us = (time.perf_counter() - t0) / 1000 * 1e6
+    rows["w2_tiny_latency"] = {"step_median_us": round(med_tiny * 1e3, 2),
+                               "host_us_per_call": round(host_us, 2),
+                               "note": "mode 0 + mode 1 of the two-rank example (65,536 B "
+                                       "per mode); host time per ABI call through Python"}
+    del xs, ys, zs
 
     # q, k and v of the timed geometry: one launch against three
     wl = wls["w8_wan720p"]
