@@ -47,7 +47,7 @@ static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrde
 #endif
 static const bool kFusedBands = ULY_FUSED_BANDS != 0;
 
-static uint32_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
+static uint64_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
     if (ULY_VBAND > 0) return ulysses::fill_relayout_vbands(p, mode, ULY_VBAND, a);
     if (ULY_BAND > 0)
         return ulysses::fill_relayout_bands(p, mode, ulysses::band_rows_for(p, mode, ULY_BAND), a);
@@ -116,8 +116,9 @@ int launch_status(hipError_t e, const char *what) {
 }
 
 // One launch covers grid_x * block threads along x; HIP bounds that by 2^32.
-int check_grid(uint32_t grid_x, uint32_t block, const char *what) {
-    if (uint64_t(grid_x) * block > 0xFFFFFFFFull)
+// grid_x comes from a 64-bit block count and is narrowed only after this.
+int check_grid(uint64_t grid_x, uint32_t block, const char *what) {
+    if (grid_x > 0xFFFFFFFFull || grid_x * block > 0xFFFFFFFFull)
         return set_error(ULYSSES_EINVAL, std::string(what) +
                                              ": one batch plane is too large for one launch");
     return ULYSSES_OK;
@@ -197,11 +198,12 @@ int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void
     rc = check_overlap(ranges);
     if (rc) return rc;
     ulysses::RelayoutArgs a;
-    const uint32_t gx = relayout_table(p, mode, &a);
+    const uint64_t gx = relayout_table(p, mode, &a);
     rc = check_grid(gx, ulysses::relayout_block_threads(), "relayout");
     if (rc) return rc;
     set_pointers(p, tensors, src, dst, &a);
-    return launch_planes(a, gx, p.b, static_cast<uint32_t>(tensors), stream, "relayout");
+    return launch_planes(a, static_cast<uint32_t>(gx), p.b, static_cast<uint32_t>(tensors),
+                         stream, "relayout");
 }
 
 }  // namespace
@@ -305,8 +307,8 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
         if (rc) return rc;
 
         ulysses::RelayoutArgs scatter, copy;
-        const uint32_t gs = relayout_table(p, mode, &scatter);
-        const uint32_t gc =
+        const uint64_t gs = relayout_table(p, mode, &scatter);
+        const uint64_t gc =
             ulysses::fill_window_copy(p, mode, ulysses::relayout_vectors_per_block(), &copy);
         rc = check_grid(gs > gc ? gs : gc, ulysses::relayout_block_threads(), "chunked relayout");
         if (rc) return rc;
@@ -319,12 +321,15 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
         for (int64_t plane = 0; plane < p.b; ++plane) {
             scatter.src_plane0 = static_cast<uint32_t>(plane);
             scatter.dst_plane0 = 0;
-            rc = launch_status(ulysses::launch_relayout(scatter, gs, 1, 1, stream),
-                               "chunk relayout");
+            rc = launch_status(
+                ulysses::launch_relayout(scatter, static_cast<uint32_t>(gs), 1, 1, stream),
+                "chunk relayout");
             if (rc) return rc;
             copy.src_plane0 = 0;
             copy.dst_plane0 = static_cast<uint32_t>(plane);
-            rc = launch_status(ulysses::launch_relayout(copy, gc, 1, 1, stream), "window copy");
+            rc = launch_status(
+                ulysses::launch_relayout(copy, static_cast<uint32_t>(gc), 1, 1, stream),
+                "window copy");
             if (rc) return rc;
         }
         return ULYSSES_OK;
@@ -370,7 +375,7 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         const uint32_t upb = ulysses::fused_units_per_block();
         const uint32_t rpb = ulysses::fused_rows_per_block(static_cast<uint32_t>(p.d));
         ulysses::RelayoutArgs t;
-        const uint32_t gx =
+        const uint64_t gx =
             rpb != 0      ? ulysses::fill_relayout_bands(p, 0, rpb, &t)
             : kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
                           : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
@@ -403,7 +408,8 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
             const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
             a.plane0 = static_cast<uint32_t>(p0);
-            rc = launch_status(ulysses::launch_fused(a, gx, static_cast<uint32_t>(n), stream),
+            rc = launch_status(ulysses::launch_fused(a, static_cast<uint32_t>(gx),
+                                                     static_cast<uint32_t>(n), stream),
                                "fused relayout");
             if (rc) return rc;
         }

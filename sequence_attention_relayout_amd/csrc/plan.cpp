@@ -168,7 +168,7 @@ uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors) {
     return static_cast<uint32_t>(t < 1 ? 1 : t);
 }
 
-uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a) {
+uint64_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];
     for (int r = 0; r < p.world; ++r) {
@@ -191,10 +191,10 @@ uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, Relayo
         a->grp_begin[grp] = static_cast<uint32_t>(blocks);
         blocks += static_cast<uint64_t>(bands) * p.world;
     }
-    return static_cast<uint32_t>(blocks);
+    return blocks;
 }
 
-uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
+uint64_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
                        RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];
@@ -216,10 +216,10 @@ uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrd
             blocks += (o.nvec + vec_per_block - 1) / vec_per_block;
             ++n;
         }
-    return static_cast<uint32_t>(blocks);
+    return blocks;
 }
 
-uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
+uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];
     for (int r = 0; r < p.world; ++r) {
@@ -242,7 +242,7 @@ uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
         a->grp_begin[grp] = static_cast<uint32_t>(blocks);
         blocks += bands * p.world;
     }
-    return static_cast<uint32_t>(blocks);
+    return blocks;
 }
 
 bool to_units(RelayoutArgs *a, uint32_t vpl) {
@@ -269,7 +269,7 @@ bool to_units(RelayoutArgs *a, uint32_t vpl) {
     return true;
 }
 
-uint32_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
+uint64_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a) {
     clear_table(a);
     const ModeGeom &g = p.mode[mode];
     a->world = 1;   // one piece per group: group r copies window r
@@ -294,7 +294,7 @@ uint32_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutA
         a->grp_begin[r] = static_cast<uint32_t>(blocks);
         blocks += (uint64_t(o.nvec) + band_vecs - 1) / band_vecs;
     }
-    return static_cast<uint32_t>(blocks);
+    return blocks;
 }
 
 }  // namespace ulysses

@@ -76,17 +76,18 @@ enum PieceOrder : int {
 
 // Launch table of one relayout pass of `mode` with `vec_per_block` 16-byte
 // vectors per block.  Pointers and plane bases are left to the caller.
-// Returns the number of blocks along grid.x (0 when nothing moves).
-uint32_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
+// Returns the number of blocks along grid.x (0 when nothing moves), as a
+// 64-bit count: the caller checks it against the launch limits before use.
+uint64_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
                        RelayoutArgs *a);
 
 // Row-band launch table of one relayout pass of `mode` (see
 // RelayoutArgs::grp_begin): bands of `band_rows` rows.  Returns grid.x.
-uint32_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a);
+uint64_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a);
 
 // Vector-band launch table: bands of `band_vecs` vectors of each piece,
 // interleaved over the group as for row bands.  Returns grid.x.
-uint32_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
+uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
 
 // Band height so that one band of the widest piece moves about
 // `target_vectors` 16-byte vectors (at least one row).
@@ -96,7 +97,7 @@ uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
 // each) into the destination shards, for the band kernel: group r holds the
 // one piece copying window r (equal row pitches on both sides), in bands of
 // `band_vecs` vectors.
-uint32_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
+uint64_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
 
 // Rescales a launch table from 16-byte vectors to units of `vpl` vectors
 // (vector counts, offsets, pitches, plane sizes and band width divided by

@@ -187,6 +187,18 @@ def test_call_errors_before_launch():
            [g, BASE + (15 << 33)], g + 64, g + 128, 1e-6, t, t + (1 << 28), 0)
 
 
+def test_launch_wider_than_grid_x_refused():
+    """8 shards of 2^30 16-byte vectors per plane: one pass needs more than
+    2^32 threads along x, which one launch cannot hold; the call refuses
+    before launching instead of truncating the block count."""
+    plan = U.ulysses_plan_create(8, 1, 8, [1 << 27] * 8, [1] * 8, "bf16")
+    assert U.ulysses_plan_bytes(plan, 0) == 2 * (1 << 30) * 8 * 16
+    src, dst = fake(8, stride=1 << 35), fake(8, stride=1 << 35, off=1 << 39)
+    for mode in (0, 1):
+        msg = expect(-1, U.ulysses_a2a_4d, plan, mode, src, dst, 0)
+        assert "one launch" in msg
+
+
 def test_multi_tensor_errors_before_launch():
     plan = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16")
     lib = U.library()
