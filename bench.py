@@ -103,7 +103,17 @@ def cpu_baseline(reps=3, budget_s=30.0):
         oracle.a2a_4d(1, 1, d, seq, head, ys_in)
         times.append(time.perf_counter() - t0)
     dt = statistics.median(times)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "cpu": cpu, "host_cores_available": len(os.sched_getaffinity(0)),
             "sample": f"the full step's geometry (W=8, 75,600 tokens, n=40, d=128, bf16): one "
                       f"mode 0 and one mode 1 on the oracle's plain index loops, single thread, "
                       f"median of {len(times)} runs of {dt:.1f} s each",
@@ -130,6 +140,8 @@ def hbm_ceilings():
             rec = json.loads(line)
             if "kernel" in rec and rec["gbs"] > res.get(rec["kernel"], 0.0):
                 res[rec["kernel"]] = rec["gbs"]   # the best launch shape of each kind
+            if "device_props" in rec:
+                res["device_props"] = rec["device_props"]
     return res or None
 
 
@@ -221,6 +233,34 @@ def main():
     m0 = [e[0].elapsed_time(e[1]) for e in evs]
     m1 = [e[1].elapsed_time(e[2]) for e in evs]
     launch_ms = statistics.mean(m0 + m1)
+
+    # The same launches with the 256 MB Infinity Cache (MALL) cold: 1 GiB is
+    # written between launches, outside the events.
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for k in range(K):
+        flush.fill_(k & 255)
+        cold[k][0].record(stream)
+        mode0()
+        cold[k][1].record(stream)
+        flush.fill_((k + 128) & 255)
+        cold[k][2].record(stream)
+        mode1()
+        cold[k][3].record(stream)
+    torch.cuda.synchronize()
+    c0 = [e[0].elapsed_time(e[1]) for e in cold]
+    c1 = [e[2].elapsed_time(e[3]) for e in cold]
+    del flush
+
+    # A second timed region like the first, for the spread between two
+    # invocations of the same K steps.
+    start.record(stream)
+    for _ in range(K):
+        mode0()
+        mode1()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step_repeat = start.elapsed_time(end) / K
     value = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = (step_bytes / 2) / (launch_ms * 1e-3) / 1e9
     log(f"step {ms_step * 1e3:.1f} us ({value:.0f} GB/s); mode 0 median "
@@ -251,9 +291,21 @@ def main():
                      "bytes_per_launch": bytes0, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "launches_timed": 2 * K,
                      "mode0_median_us": round(statistics.median(m0) * 1e3, 2),
-                     "mode1_median_us": round(statistics.median(m1) * 1e3, 2)},
+                     "mode1_median_us": round(statistics.median(m1) * 1e3, 2),
+                     "mode0_min_us": round(min(m0) * 1e3, 2),
+                     "mode1_min_us": round(min(m1) * 1e3, 2),
+                     "mode0_mall_cold_median_us": round(statistics.median(c0) * 1e3, 2),
+                     "mode1_mall_cold_median_us": round(statistics.median(c1) * 1e3, 2)},
+        "ms_per_step_repeat": round(ms_step_repeat, 5),
+        "step_spread_pct": round(100 * abs(ms_step_repeat - ms_step) / ms_step, 2),
         "d2d_copy_ceiling_gbs": round(d2d, 1),
     }
+    if ceilings and "device_props" in ceilings:
+        # 2 x memory clock x bus width as the runtime reports them; on this
+        # part the reported clock does not give HBM3E's data rate, so the
+        # figure sits below the measured read ceiling and is not the peak
+        # the fraction is taken against.
+        result["device_props_hbm"] = ceilings.pop("device_props")
     if ceilings:
         result["hbm_ceilings_gbs"] = ceilings
         if "copy" in ceilings:

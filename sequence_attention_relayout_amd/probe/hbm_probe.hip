@@ -60,6 +60,18 @@ __global__ void __launch_bounds__(B) write_kernel(u32x4 *__restrict__ d, size_t 
 }
 
 int main() {
+    // The peak the runtime reports: memory clock (kHz) x bus width, two
+    // transfers per clock.
+    {
+        hipDeviceProp_t prop;
+        CHECK(hipGetDeviceProperties(&prop, 0));
+        const double peak = 2.0 * double(prop.memoryClockRate) * 1e3 *
+                            double(prop.memoryBusWidth) / 8.0 / 1e9;
+        std::printf("{\"device_props\": {\"memory_clock_khz\": %d, \"memory_bus_bits\": %d, "
+                    "\"peak_gbs\": %.1f}}\n",
+                    prop.memoryClockRate, prop.memoryBusWidth, peak);
+        std::fflush(stdout);
+    }
     const size_t moved = 1548288000ull;
     const size_t n_all = moved / 16;   // vectors read (or written) by the one-sided kernels
     const size_t n_copy = n_all / 2;   // vectors read and written by the copy
