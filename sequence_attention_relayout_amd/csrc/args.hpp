@@ -31,8 +31,35 @@ struct PieceArgs {
     uint32_t src_row0;    // sequence position of the piece's first source row
                           // (global position of row 0; used by the fused path)
     uint8_t j, r;         // source and destination rank
-    uint8_t pad[2];
+    uint8_t vpr_s1, vpr_s2;   // shifts of the exact division by vpr (div32)
+    uint32_t vpr_m;           // multiplier of the exact division by vpr (div32)
 };
+
+// floor(n / d) for every 32-bit n, from the multiplier and shifts that
+// div32_magic gives for d (Granlund & Montgomery, "Division by invariant
+// integers using multiplication", 1994, Figure 4.1).  constexpr, so the HIP
+// kernels call the same function; on the GPU a block-uniform n compiles to
+// scalar instructions.
+constexpr uint32_t div32(uint32_t n, uint32_t m, uint32_t s1, uint32_t s2) {
+    const uint32_t t = static_cast<uint32_t>((uint64_t{n} * m) >> 32);
+    return (t + ((n - t) >> s1)) >> s2;
+}
+
+struct Div32Magic {
+    uint32_t m;
+    uint8_t s1, s2;
+};
+
+// Multiplier and shifts of div32 for a divisor 1 <= d <= 2^31:
+// l = ceil(log2 d), m = floor(2^32 * (2^l - d) / d) + 1, s1 = min(l, 1),
+// s2 = max(l - 1, 0).
+constexpr Div32Magic div32_magic(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t{1} << l) < d) ++l;
+    const uint64_t m = ((uint64_t{1} << 32) * ((uint64_t{1} << l) - d)) / d + 1;
+    return Div32Magic{static_cast<uint32_t>(m), static_cast<uint8_t>(l > 0 ? 1 : 0),
+                      static_cast<uint8_t>(l > 0 ? l - 1 : 0)};
+}
 
 // Launch table for one relayout pass: grid.x walks the pieces' blocks, grid.y
 // the batch planes, grid.z the tensors (all of one plan's geometry).  Block x
@@ -83,6 +110,9 @@ struct FusedArgs {
     uint32_t grp_begin[kMaxWorld];
     uint32_t world;
     uint32_t band_vecs;
+    // exact division by world (div32): a block's band within its group
+    uint32_t world_m;
+    uint32_t world_s1, world_s2;
 };
 
 static_assert(sizeof(RelayoutArgs) <= 4096, "kernel argument block over 4 KiB");

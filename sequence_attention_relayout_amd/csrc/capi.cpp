@@ -370,13 +370,15 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         rc = check_overlap(ranges);
         if (rc) return rc;
 
-        // one lane moves `vpl` consecutive vectors of a head row
-        const uint32_t vpl = ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
+        // d = 128: the band kernel, bands of `bv` 16-byte vectors; other d:
+        // fused_kernel, one lane moving `vpl` consecutive vectors of a head row
+        const uint32_t bv = ulysses::fused_band_vectors(static_cast<uint32_t>(p.d));
+        const uint32_t vpl =
+            bv != 0 ? 1 : ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
         const uint32_t upb = ulysses::fused_units_per_block();
-        const uint32_t rpb = ulysses::fused_rows_per_block(static_cast<uint32_t>(p.d));
         ulysses::RelayoutArgs t;
         const uint64_t gx =
-            rpb != 0      ? ulysses::fill_relayout_bands(p, 0, rpb, &t)
+            bv != 0       ? ulysses::fill_relayout_vbands(p, 0, bv, &t)
             : kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
                           : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
         if (!ulysses::to_units(&t, vpl))
@@ -396,6 +398,10 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         std::memcpy(a.grp_begin, t.grp_begin, sizeof a.grp_begin);
         a.world = t.world;
         a.band_vecs = t.band_vecs;
+        const ulysses::Div32Magic wm = ulysses::div32_magic(t.world > 0 ? t.world : 1);
+        a.world_m = wm.m;
+        a.world_s1 = wm.s1;
+        a.world_s2 = wm.s2;
         a.gamma[0] = gamma_q;
         a.gamma[1] = gamma_k;
         a.rope_cos = rope_cos;

@@ -53,20 +53,14 @@
 #ifndef ULY_FUSED_VPL
 #define ULY_FUSED_VPL 1
 #endif
-// Row-wise fused kernel for d = 128 (one table read per destination row).
-#ifndef ULY_FUSED_ROWS
-#define ULY_FUSED_ROWS 1
-#endif
-#ifndef ULY_FUSED_ROWS_BLOCK
-#define ULY_FUSED_ROWS_BLOCK 64
-#endif
-// heads of a row handled per divide/sqrt sequence (at most 8)
-#ifndef ULY_FUSED_HC
-#define ULY_FUSED_HC 8
-#endif
 // Share one divide/sqrt sequence between the unroll slots of a 16-lane row.
 #ifndef ULY_FUSED_SHARE_INV
 #define ULY_FUSED_SHARE_INV 1
+#endif
+// Vectors per lane of the band kernel for d = 128 (1, 2 or 4; each lane
+// handles that many head rows of q and as many of k).  One measured best.
+#ifndef ULY_FUSED_BAND_UNROLL
+#define ULY_FUSED_BAND_UNROLL 1
 #endif
 
 namespace ulysses {
@@ -423,126 +417,167 @@ __global__ void __launch_bounds__(BLOCK) fused_kernel(const FusedArgs a) {
     }
 }
 
-// Row-wise form for d = 128 (16 lanes per head row): a 16-lane group owns one
-// destination row of one piece and walks its heads, so the rotary table of
-// the row (cos and sin of the row's position, 16 bytes each per lane) is
-// read once for all H_r heads instead of once per head, and lane k of the
-// group computes head k's 1/sqrt(ms + eps) for up to HC heads at a time,
-// handed to the group with DPP row_newbcast:k.  Operation order and rounding
-// are those of fused_kernel.  Blocks take row bands of BLOCK/16 rows,
-// interleaved over the pieces sharing a source shard.
-template <int BLOCK, int HC>
-__global__ void __launch_bounds__(BLOCK) fused_rows_kernel(const FusedArgs a) {
-    constexpr uint32_t kRowsPerBlock = BLOCK / 16;
-    const uint32_t x = blockIdx.x;
+// Block order that puts the W consecutive blocks of one band (the pieces of
+// one band) on one XCD.  Workgroups go round-robin over the 8 XCDs by linear
+// id, so within each run of 8 bands (8*W blocks) physical block x takes band
+// 8c + (x mod 8) and piece (x mod 8W) / 8; the last, partial run keeps the
+// identity order.  A bijection on [0, n); x / (8W) is taken as (x / 8) / W
+// through the exact division by W.
+__device__ __forceinline__ uint32_t band_xcd_order(uint32_t x, uint32_t n, const FusedArgs &a) {
+    const uint32_t w = a.world;
+    // x / (8w) == (x / 8) / w, through the exact division by w
+    const uint32_t full = div32(n >> 3, a.world_m, a.world_s1, a.world_s2) * (8 * w);
+    if (x >= full) return x;
+    const uint32_t c = div32(x >> 3, a.world_m, a.world_s1, a.world_s2);
+    const uint32_t rem = x - c * (8 * w);
+    return (8 * c + (rem & 7)) * w + (rem >> 3);
+}
+
+// Band form for d = 128, with the relayout kernel's access shape: a one-wave
+// block takes one band of 64 * UNROLL consecutive vectors of a piece, UNROLL
+// vectors per lane 64 apart, 16 lanes per head row, and moves that band of
+// both q and k, so the band's rotary entries are read once for the two.
+// Blocks follow band_xcd_order: the W pieces of a band share an XCD, and
+// with it the L2 that holds their rotary rows.  Everything block-uniform (the
+// piece, the band's first row and column, the base addresses of sources,
+// destinations and rotary rows) is computed once per block with scalar
+// instructions, the divisions by runtime values through host-computed exact
+// multipliers (div32); each lane then adds 32-bit offsets.  Lanes past the
+// end of a piece reload its last vector and skip their stores, so no lane
+// works on uninitialised registers and no load is predicated.  Operation
+// order and rounding are those of fused_kernel; the 2 * UNROLL rows of a
+// lane share one divide/sqrt sequence (lane i of each 16-lane row computes
+// the i-th and DPP row_newbcast:i hands it out).
+template <int UNROLL>
+__global__ void __launch_bounds__(64) fused_band_kernel(const FusedArgs a) {
+    static_assert(UNROLL == 1 || UNROLL == 2 || UNROLL == 4, "slots per lane");
+    constexpr int T = 2;                         // q and k
+    constexpr int S = T * UNROLL;                // rows per lane sharing one 1/sqrt pass
+    static_assert(S <= 8, "at most 8 slots share the divide/sqrt sequence");
+    constexpr uint32_t kBand = 64 * UNROLL;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t x = band_xcd_order(blockIdx.x, gridDim.x, a);
     uint32_t g = 0;
 #pragma unroll
     for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
     const uint32_t local = x - a.grp_begin[g];
-    const uint32_t band = local / a.world;
+    const uint32_t band = div32(local, a.world_m, a.world_s1, a.world_s2);
     const PieceArgs pc = a.piece[g * a.world + (local - band * a.world)];
-    if (pc.vpr == 0) return;                     // empty piece (no heads)
-    const uint32_t rows = pc.nvec / pc.vpr;      // uniform
-    const uint32_t row0 = band * kRowsPerBlock;
-    if (row0 >= rows) return;                    // uniform: band past the piece
-    const uint32_t heads = pc.vpr / 16;
-    const uint32_t lane = threadIdx.x & 15;
-    const uint32_t row = row0 + threadIdx.x / 16;
-    const bool row_ok = row < rows;              // uniform per 16-lane group
+    const uint32_t s0 = band * kBand;
+    if (s0 >= pc.nvec) return;                   // uniform: band past the piece (or empty)
+    const uint32_t last = min(kBand, pc.nvec - s0) - 1;   // last valid lane index
+    const uint32_t row0 = div32(s0, pc.vpr_m, pc.vpr_s1, pc.vpr_s2);
+    const uint32_t col0 = s0 - row0 * pc.vpr;
     const uint64_t plane = uint64_t(a.plane0) + blockIdx.y;
-    const uint64_t src_vec = plane * a.src_plane[pc.j] + pc.src_off +
-                             uint64_t(row) * pc.src_pitch + lane;
-    const uint64_t dst_vec = plane * a.dst_plane[pc.r] + pc.dst_off +
-                             uint64_t(row) * pc.dst_pitch + lane;
-
-    // the row's rotary entries (pairs 4*lane .. +3), read once for every
-    // head of the row
-    f32x4 cv = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
-    if (row_ok) {
-        const uint64_t tab = uint64_t(pc.src_row0 + row) * 64 + 4 * lane;
-        cv = *reinterpret_cast<const f32x4 *>(a.rope_cos + tab);
-        sv = *reinterpret_cast<const f32x4 *>(a.rope_sin + tab);
+    const uint64_t src_v = plane * a.src_plane[pc.j] + pc.src_off + uint64_t(row0) * pc.src_pitch;
+    const uint64_t dst_v = plane * a.dst_plane[pc.r] + pc.dst_off + uint64_t(row0) * pc.dst_pitch;
+    const uint32_t t0 = 0;
+    const unsigned char *sb[T];
+    unsigned char *db[T];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+        sb[tt] = a.src[t0 + tt][pc.j] + (src_v << 4);
+        db[tt] = a.dst[t0 + tt][pc.r] + (dst_v << 4);
     }
-    const float c[4] = {cv.x, cv.y, cv.z, cv.w};
-    const float sn[4] = {sv.x, sv.y, sv.z, sv.w};
+    const uint64_t trow = uint64_t(pc.src_row0 + row0) * 64;   // global position * d/2
+    const unsigned char *cb = reinterpret_cast<const unsigned char *>(a.rope_cos + trow);
+    const unsigned char *snb = reinterpret_cast<const unsigned char *>(a.rope_sin + trow);
+    const uint32_t lane = tid & 15;
+
+    float gm[T][8];
+#pragma unroll
+    for (int tt = 0; tt < T; ++tt) {
+        const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[t0 + tt] + 8 * lane);
+        const f32x4 g0 = gp[0], g1 = gp[1];
+        gm[tt][0] = g0.x; gm[tt][1] = g0.y; gm[tt][2] = g0.z; gm[tt][3] = g0.w;
+        gm[tt][4] = g1.x; gm[tt][5] = g1.y; gm[tt][6] = g1.z; gm[tt][7] = g1.w;
+    }
     const float eps = a.eps;
     const float inv_d = a.inv_d;
 
+    u32x4 xv[T][UNROLL];
+    f32x4 cv[UNROLL], sv[UNROLL];
+    uint32_t doff[UNROLL];
+    bool ok[UNROLL];
+#pragma unroll
+    for (int k = 0; k < UNROLL; ++k) {
+        const uint32_t lin = tid + uint32_t(k * 64);
+        ok[k] = lin <= last;
+        // below 2^16: col0 < vpr <= 32768 and lin < kBand
+        const uint32_t t = col0 + min(lin, last);
+        const uint32_t dr = div_vpr(t, pc.vpr, pc.magic);   // rows past row0
+        // 24-bit products and 32-bit byte offsets: a head row is 16 vectors,
+        // so dr <= kBand / 16 <= 16, and pitches and vpr are at most 32768
+        // vectors; every offset stays below 17 rows of 512 KiB
+        const uint32_t col = t - __umul24(dr, pc.vpr);
+        const uint32_t soff = (__umul24(dr, pc.src_pitch) + col) << 4;
+        doff[k] = (__umul24(dr, pc.dst_pitch) + col) << 4;
+        const uint32_t toff = (dr * 64 + 4 * lane) * 4;
+#pragma unroll
+        for (int tt = 0; tt < T; ++tt) xv[tt][k] = load16<true>(sb[tt] + soff);
+        cv[k] = *reinterpret_cast<const f32x4 *>(cb + toff);
+        sv[k] = *reinterpret_cast<const f32x4 *>(snb + toff);
+    }
+    // every load of the block is in flight before any arithmetic starts
+    __builtin_amdgcn_sched_barrier(0);
+    float ss[S];
+#pragma unroll
+    for (int i = 0; i < S; ++i) {
+        const u32x4 v = xv[i / UNROLL][i % UNROLL];
+        const float xf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xf[e], xf[e], part);
+        ss[i] = group_sum<16>(part);
+    }
+    // lane i of each 16-lane row computes slot i's 1/sqrt(ms + eps) and DPP
+    // row_newbcast:i hands it to the row (the same operations on the same
+    // value, so the same bits as every lane computing its own)
+    float invs[S];
     {
-        const uint32_t tensor = blockIdx.z;
-        const unsigned char *src = a.src[tensor][pc.j] + src_vec * 16;
-        unsigned char *dst = a.dst[tensor][pc.r] + dst_vec * 16;
-        const f32x4 *gp = reinterpret_cast<const f32x4 *>(a.gamma[tensor] + 8 * lane);
-        const f32x4 g0 = gp[0], g1 = gp[1];
-        const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-
-        for (uint32_t h0 = 0; h0 < heads; h0 += HC) {
-            const uint32_t cnt = min(uint32_t(HC), heads - h0);   // uniform
-            u32x4 xv[HC];
-            float ss[HC];
+        float sel = ss[0];
 #pragma unroll
-            for (int i = 0; i < HC; ++i) {
-                xv[i] = u32x4{0, 0, 0, 0};
-                if (row_ok && uint32_t(i) < cnt) xv[i] = load16<true>(src + (h0 + i) * 256);
-            }
+        for (int i = 1; i < S; ++i) sel = (lane == uint32_t(i)) ? ss[i] : sel;
+        const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
+        invs[0] = dpp<0x150>(mine);
+        if constexpr (S > 1) invs[1] = dpp<0x151>(mine);
+        if constexpr (S > 2) invs[2] = dpp<0x152>(mine);
+        if constexpr (S > 3) invs[3] = dpp<0x153>(mine);
+        if constexpr (S > 4) invs[4] = dpp<0x154>(mine);
+        if constexpr (S > 5) invs[5] = dpp<0x155>(mine);
+        if constexpr (S > 6) invs[6] = dpp<0x156>(mine);
+        if constexpr (S > 7) invs[7] = dpp<0x157>(mine);
+    }
 #pragma unroll
-            for (int i = 0; i < HC; ++i) {
-                const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
-                                     bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
-                                     bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
-                float part = 0.0f;
+    for (int i = 0; i < S; ++i) {
+        const int tt = i / UNROLL, k = i % UNROLL;
+        const u32x4 v = xv[tt][k];
+        const float xf[8] = {bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y),
+                             bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w)};
+        const float cc[4] = {cv[k].x, cv[k].y, cv[k].z, cv[k].w};
+        const float sn[4] = {sv[k].x, sv[k].y, sv[k].z, sv[k].w};
+        float y[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xf[e], xf[e], part);
-                ss[i] = group_sum<16>(part);
-            }
-            // lane k of the group takes head k; every lane of the group holds
-            // the same ss of every head, so the broadcast value is the one
-            // each lane would have computed itself.  ms = ss * (1/d) equals
-            // ss / d exactly.
-            float sel = ss[0];
+        for (int e = 0; e < 8; ++e) y[e] = (xf[e] * invs[i]) * gm[tt][e];
+        uint32_t o[4];
 #pragma unroll
-            for (int i = 1; i < HC; ++i) sel = (lane == uint32_t(i)) ? ss[i] : sel;
-            const float mine = 1.0f / __builtin_sqrtf(sel * inv_d + eps);
-            float invs[HC];
-            invs[0] = dpp<0x150>(mine);
-            if constexpr (HC > 1) invs[1] = dpp<0x151>(mine);
-            if constexpr (HC > 2) invs[2] = dpp<0x152>(mine);
-            if constexpr (HC > 3) invs[3] = dpp<0x153>(mine);
-            if constexpr (HC > 4) invs[4] = dpp<0x154>(mine);
-            if constexpr (HC > 5) invs[5] = dpp<0x155>(mine);
-            if constexpr (HC > 6) invs[6] = dpp<0x156>(mine);
-            if constexpr (HC > 7) invs[7] = dpp<0x157>(mine);
-#pragma unroll
-            for (int i = 0; i < HC; ++i) {
-                const float xf[8] = {bf16_lo(xv[i].x), bf16_hi(xv[i].x), bf16_lo(xv[i].y),
-                                     bf16_hi(xv[i].y), bf16_lo(xv[i].z), bf16_hi(xv[i].z),
-                                     bf16_lo(xv[i].w), bf16_hi(xv[i].w)};
-                float y[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) y[e] = (xf[e] * invs[i]) * gm[e];
-                uint32_t o[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float e0 = y[2 * q] * c[q];
-                    const float e1 = y[2 * q + 1] * sn[q];
-                    const float e2 = y[2 * q] * sn[q];
-                    const float e3 = y[2 * q + 1] * c[q];
-                    o[q] = pack_bf16x2(e0 - e1, e2 + e3);
-                }
-                if (row_ok && uint32_t(i) < cnt)
-                    store16<true>(dst + (h0 + i) * 256, u32x4{o[0], o[1], o[2], o[3]});
-            }
+        for (int q = 0; q < 4; ++q) {
+            const float e0 = y[2 * q] * cc[q];
+            const float e1 = y[2 * q + 1] * sn[q];
+            const float e2 = y[2 * q] * sn[q];
+            const float e3 = y[2 * q + 1] * cc[q];
+            o[q] = pack_bf16x2(e0 - e1, e2 + e3);
         }
+        if (ok[k]) store16<true>(db[tt] + doff[k], u32x4{o[0], o[1], o[2], o[3]});
     }
 }
 
-uint32_t fused_rows_per_block(uint32_t d) {
-    return (ULY_FUSED_ROWS && d == 128) ? ULY_FUSED_ROWS_BLOCK / 16 : 0;
-}
+uint32_t fused_band_vectors(uint32_t d) { return d == 128 ? 64 * ULY_FUSED_BAND_UNROLL : 0; }
 
 uint32_t fused_units_per_block() { return ULY_FUSED_BLOCK * ULY_FUSED_UNROLL; }
 uint32_t fused_block_threads(uint32_t d) {
-    return fused_rows_per_block(d) != 0 ? ULY_FUSED_ROWS_BLOCK : ULY_FUSED_BLOCK;
+    return fused_band_vectors(d) != 0 ? 64 : ULY_FUSED_BLOCK;
 }
 
 uint32_t fused_vectors_per_lane(uint32_t d) {
@@ -577,13 +612,11 @@ static hipError_t launch_fused_vpl(const FusedArgs &a, uint32_t grid_x, uint32_t
 hipError_t launch_fused(const FusedArgs &a, uint32_t grid_x, uint32_t planes,
                         hipStream_t stream) {
     if (grid_x == 0 || planes == 0) return hipSuccess;
-    if (fused_rows_per_block(a.d) != 0) {
-        void *argv[] = {const_cast<FusedArgs *>(&a)};
+    void *argv[] = {const_cast<FusedArgs *>(&a)};
+    if (fused_band_vectors(a.d) != 0)   // q and k in one block: grid.z = 1
         return hipLaunchKernel(
-            reinterpret_cast<const void *>(
-                &fused_rows_kernel<ULY_FUSED_ROWS_BLOCK, ULY_FUSED_HC>),
-            dim3(grid_x, planes, 2), dim3(ULY_FUSED_ROWS_BLOCK, 1, 1), argv, 0, stream);
-    }
+            reinterpret_cast<const void *>(&fused_band_kernel<ULY_FUSED_BAND_UNROLL>),
+            dim3(grid_x, planes, 1), dim3(64, 1, 1), argv, 0, stream);
     switch (fused_vectors_per_lane(a.d)) {
     case 1: return launch_fused_vpl<1>(a, grid_x, planes, stream);
 #if ULY_FUSED_VPL >= 2

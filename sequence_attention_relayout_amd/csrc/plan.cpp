@@ -137,6 +137,14 @@ int plan_build(Plan *p, int world, int64_t b, int64_t d, const int64_t *seq_spli
     return kOk;
 }
 
+// The exact 32-bit division by o->vpr (a piece without rows keeps d = 1).
+static void set_vpr_division(PieceArgs *o) {
+    const Div32Magic dm = div32_magic(o->vpr > 0 ? o->vpr : 1);
+    o->vpr_m = dm.m;
+    o->vpr_s1 = dm.s1;
+    o->vpr_s2 = dm.s2;
+}
+
 static void fill_piece_args(const Piece &pc, PieceArgs *o) {
     const uint32_t vpr = static_cast<uint32_t>(pc.row_bytes / 16);
     o->vpr = vpr;
@@ -149,7 +157,7 @@ static void fill_piece_args(const Piece &pc, PieceArgs *o) {
     o->src_row0 = static_cast<uint32_t>(pc.seq_pos0);
     o->j = static_cast<uint8_t>(pc.j);
     o->r = static_cast<uint8_t>(pc.r);
-    o->pad[0] = o->pad[1] = 0;
+    set_vpr_division(o);
 }
 
 static void clear_table(RelayoutArgs *a) {
@@ -265,6 +273,7 @@ bool to_units(RelayoutArgs *a, uint32_t vpl) {
         o.src_off /= vpl;
         o.dst_off /= vpl;
         o.magic = row_magic(o.vpr);
+        set_vpr_division(&o);
     }
     return true;
 }

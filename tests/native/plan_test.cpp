@@ -10,7 +10,8 @@
 //   - the window copy of the plane-at-a-time mode covers each destination
 //     plane once from the same offset in the window;
 //   - the fused path's lane of a vector within its head row is the thread's
-//     lane modulo d/8;
+//     lane modulo d/8, and the band kernel's block order, exact divisions
+//     and 32-bit offsets are valid;
 //   - the multiply-high division by the row length is exact at every
 //     quotient boundary, hence everywhere (both sides are monotone).
 // Prints "OK <checks>" and exits 0, or a message and exits 1.
@@ -286,58 +287,115 @@ static void check_fused_units(int world, int64_t b, int64_t d, const std::vector
     }
 }
 
-// The row-wise fused kernel (d = 128): block x of a row-band table with
-// `rpb` rows per block; a 16-lane group owns one row of the piece and walks
-// its heads.  Every destination vector once, from the defined source, and
-// the rotary position is the row's global position.
-static void check_fused_rows(int world, int64_t b, const std::vector<int64_t> &S,
-                             const std::vector<int64_t> &H, uint32_t rpb) {
+// The band kernel of the fused path (d = 128): a vector-band table with
+// 64 * unroll vectors per band, blocks taken in the XCD-aware order, each
+// block moving its band of q and of k (the same offsets for both).  Checks
+// that the order is a bijection, the exact divisions agree with '/', every
+// destination vector is written once from the defined source, the rotary
+// row is the row's global position, and the kernel's 32-bit byte offsets and
+// 16-bit division numerators stay in range.
+static uint32_t band_xcd_order(uint32_t x, uint32_t n, uint32_t w, const Div32Magic &dm) {
+    const uint32_t full = div32(n >> 3, dm.m, dm.s1, dm.s2) * (8 * w);
+    if (x >= full) return x;
+    const uint32_t c = div32(x >> 3, dm.m, dm.s1, dm.s2);
+    const uint32_t rem = x - c * (8 * w);
+    return (8 * c + (rem & 7)) * w + (rem >> 3);
+}
+
+static void check_fused_band(int world, int64_t b, const std::vector<int64_t> &S,
+                             const std::vector<int64_t> &H, uint32_t unroll) {
     Plan p;
     std::string msg;
     REQUIRE(plan_build(&p, world, b, 128, S.data(), H.data(), 0, 0, &msg) == kOk, "plan");
     const int64_t hv = 16, n_global = p.n_global, s_global = p.s_global;
+    const uint32_t band_v = 64 * unroll;
     RelayoutArgs a;
-    const uint32_t gx = fill_relayout_bands(p, 0, rpb, &a);
+    const uint64_t gx64 = fill_relayout_vbands(p, 0, band_v, &a);
+    REQUIRE(to_units(&a, 1), "to_units");
+    REQUIRE(gx64 % a.world == 0, "band table not a multiple of world");
+    const uint32_t gx = static_cast<uint32_t>(gx64);
+    const Div32Magic wm = div32_magic(a.world);
+    std::vector<int> order_hits(gx, 0);
     std::vector<std::vector<int>> hits(world);
     for (int r = 0; r < world; ++r)
         hits[r].assign(static_cast<size_t>(b * p.mode[0].dst_plane[r] / 16), 0);
     for (uint32_t y = 0; y < b; ++y)
-        for (uint32_t x = 0; x < gx; ++x) {
+        for (uint32_t xb = 0; xb < gx; ++xb) {
+            const uint32_t x = band_xcd_order(xb, gx, a.world, wm);
+            REQUIRE(x < gx, "block order past the grid");
+            if (y == 0) order_hits[x] += 1;
             uint32_t g = 0;
             for (int q = 1; q < kMaxWorld; ++q) g += a.grp_begin[q] <= x ? 1u : 0u;
             const uint32_t local = x - a.grp_begin[g];
-            const uint32_t band = local / a.world;
+            const uint32_t band = div32(local, wm.m, wm.s1, wm.s2);
+            REQUIRE(band == local / a.world, "band division");
             const PieceArgs &pc = a.piece[g * a.world + (local - band * a.world)];
-            if (pc.vpr == 0) continue;
-            const uint32_t rows = pc.nvec / pc.vpr, heads = pc.vpr / 16;
-            if (band * rpb >= rows) continue;
-            for (uint32_t t = 0; t < rpb * 16; ++t) {
-                const uint32_t lane = t & 15, row = band * rpb + t / 16;
-                if (row >= rows) continue;
-                for (uint32_t h = 0; h < heads; ++h) {
-                    const uint64_t sv = uint64_t(y) * a.src_plane[pc.j] + pc.src_off +
-                                        uint64_t(row) * pc.src_pitch + lane + h * 16;
-                    const uint64_t dvv = uint64_t(y) * a.dst_plane[pc.r] + pc.dst_off +
-                                         uint64_t(row) * pc.dst_pitch + lane + h * 16;
-                    REQUIRE(dvv < hits[pc.r].size(), "rows kernel past shard");
-                    hits[pc.r][dvv] += 1;
-                    int64_t dv = static_cast<int64_t>(dvv);
-                    const int64_t e = dv % hv; dv /= hv;
-                    const int64_t hh = dv % p.H[pc.r]; dv /= p.H[pc.r];
-                    const int64_t Sg = dv % s_global, bi = dv / s_global;
-                    int j = 0;
-                    while (!(p.seq_off[j] <= Sg && Sg < p.seq_off[j + 1])) ++j;
-                    const int64_t want = ((bi * p.S[j] + (Sg - p.seq_off[j])) * n_global +
-                                          p.head_off[pc.r] + hh) * hv + e;
-                    REQUIRE(pc.j == j && int64_t(sv) == want, "rows kernel source");
-                    REQUIRE(int64_t(pc.src_row0) + int64_t(row) == Sg, "rows kernel position");
-                    REQUIRE(int64_t(lane) == e, "rows kernel lane");
-                }
+            const uint32_t s0 = band * band_v;
+            if (s0 >= pc.nvec) continue;
+            const uint32_t last = std::min(band_v, pc.nvec - s0) - 1;
+            const uint32_t row0 = div32(s0, pc.vpr_m, pc.vpr_s1, pc.vpr_s2);
+            REQUIRE(row0 == s0 / pc.vpr, "row division");
+            const uint32_t col0 = s0 - row0 * pc.vpr;
+            for (uint32_t lin = 0; lin < band_v; ++lin) {
+                const bool ok = lin <= last;
+                const uint32_t t = col0 + std::min(lin, last);
+                REQUIRE(t < 65536u, "band numerator %u out of range", t);
+                const uint32_t dr = pc.vpr == 1 ? t : umulhi(t, pc.magic);
+                REQUIRE(dr == t / pc.vpr, "row split");
+                REQUIRE(dr <= band_v / 16, "band spans %u rows", dr + 1);
+                const uint32_t col = t - dr * pc.vpr;
+                const uint64_t soff = (uint64_t(dr) * pc.src_pitch + col) << 4;
+                const uint64_t doff = (uint64_t(dr) * pc.dst_pitch + col) << 4;
+                REQUIRE(soff < (uint64_t{1} << 32) && doff < (uint64_t{1} << 32),
+                        "32-bit offsets");
+                // lanes past the piece reload its last vector and store
+                // nothing; valid lanes come in whole 16-lane rows
+                if (!ok) continue;
+                REQUIRE(col % 16 == (lin & 15), "band lane within its head row");
+                REQUIRE(lin / 16 * 16 + 15 <= last, "16-lane row partly past the piece");
+                const uint32_t row = row0 + dr;
+                const uint64_t sv = uint64_t(y) * a.src_plane[pc.j] + pc.src_off +
+                                    uint64_t(row) * pc.src_pitch + col;
+                const uint64_t dvv = uint64_t(y) * a.dst_plane[pc.r] + pc.dst_off +
+                                     uint64_t(row) * pc.dst_pitch + col;
+                REQUIRE(dvv < hits[pc.r].size(), "band kernel past shard");
+                hits[pc.r][dvv] += 1;
+                int64_t dv = static_cast<int64_t>(dvv);
+                const int64_t e = dv % hv; dv /= hv;
+                const int64_t hh = dv % p.H[pc.r]; dv /= p.H[pc.r];
+                const int64_t Sg = dv % s_global, bi = dv / s_global;
+                int j = 0;
+                while (!(p.seq_off[j] <= Sg && Sg < p.seq_off[j + 1])) ++j;
+                const int64_t want = ((bi * p.S[j] + (Sg - p.seq_off[j])) * n_global +
+                                      p.head_off[pc.r] + hh) * hv + e;
+                REQUIRE(pc.j == j && int64_t(sv) == want, "band kernel source");
+                REQUIRE(int64_t(pc.src_row0) + int64_t(row) == Sg, "band kernel position");
             }
         }
+    for (uint32_t x = 0; x < gx; ++x) REQUIRE(order_hits[x] == 1, "block order not a bijection");
     for (int r = 0; r < world; ++r)
         for (size_t i = 0; i < hits[r].size(); ++i)
-            REQUIRE(hits[r][i] == 1, "rows kernel coverage rank %d vec %zu: %d", r, i, hits[r][i]);
+            REQUIRE(hits[r][i] == 1, "band kernel coverage rank %d vec %zu: %d", r, i, hits[r][i]);
+}
+
+// The exact 32-bit division against '/', at quotient boundaries and at random.
+static void check_div32(std::mt19937_64 &rng) {
+    std::vector<uint32_t> ds;
+    for (uint32_t v = 1; v <= 4096; ++v) ds.push_back(v);
+    for (int i = 0; i < 2000; ++i) ds.push_back(1 + static_cast<uint32_t>(rng() % 0x80000000u));
+    ds.push_back(0x80000000u);
+    for (uint32_t v : ds) {
+        const Div32Magic dm = div32_magic(v);
+        const uint32_t probes[] = {0u, 1u, v - 1, v, v + 1, 0xFFFFFFFFu, 0xFFFFFFFFu - v,
+                                   0x80000000u, static_cast<uint32_t>(rng()),
+                                   static_cast<uint32_t>(rng())};
+        for (uint32_t n : probes) REQUIRE(div32(n, dm.m, dm.s1, dm.s2) == n / v, "div32 %u / %u", n, v);
+        for (uint64_t k = 1; k * v <= 0xFFFFFFFFull && k < 64; ++k) {
+            const uint32_t lo = static_cast<uint32_t>(k * v - 1), hi = static_cast<uint32_t>(k * v);
+            REQUIRE(div32(lo, dm.m, dm.s1, dm.s2) == k - 1 && div32(hi, dm.m, dm.s1, dm.s2) == k,
+                    "div32 boundary %u", v);
+        }
+    }
 }
 
 static void check_errors() {
@@ -414,8 +472,12 @@ int main() {
         }
         S[0] += 1;
         H[world - 1] += 1;
-        check_fused_rows(world, 1 + static_cast<int64_t>(rng() % 2), S, H, it % 2 ? 4 : 8);
+        check_fused_band(world, 1 + static_cast<int64_t>(rng() % 2), S, H, 1u << (it % 3));
     }
+    // many equal pieces: full runs of 8 bands in the XCD order, and a tail
+    check_fused_band(8, 1, std::vector<int64_t>(8, 40), std::vector<int64_t>(8, 5), 1);
+    check_fused_band(7, 2, {9, 40, 3, 17, 0, 22, 31}, {6, 6, 6, 6, 6, 5, 5}, 2);
+    check_div32(rng);
     std::printf("OK %ld\n", g_checks);
     return 0;
 }

@@ -434,8 +434,9 @@ def test_fused_medium_full_compare(d, world, seq_total):
 
 @pytest.mark.parametrize("world,heads", [(2, [12, 9]), (1, [20]), (3, [17, 0, 8])])
 def test_fused_many_heads_full_compare(world, heads):
-    """More than 8 heads per rank: the row-wise d=128 kernel walks its heads
-    in several chunks."""
+    """Many heads per rank (and a rank with none): with d = 128 a band of
+    the fused band kernel spans several head rows of a piece row, or several
+    piece rows when the rank has few heads."""
     seq = W.seeded_partition(7, 300, world) if world > 1 else [300]
     H.say(f"case: fused many heads W={world} seq={seq} head={heads}")
     plan = U.ulysses_plan_create(world, 2, 128, seq, heads, "bf16")
