@@ -45,10 +45,17 @@ def log(msg):
 
 
 def kernel_source_hash():
+    """SHA-256 of the kernel sources with comments and layout removed, so a
+    counter summary stays attached to the code it measured and edits to
+    comments alone do not detach it."""
+    import re
     h = hashlib.sha256()
     for f in ("kernels.hip", "args.hpp"):
-        with open(os.path.join(ROOT, "sequence_attention_relayout_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "sequence_attention_relayout_amd", "csrc", f)) as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

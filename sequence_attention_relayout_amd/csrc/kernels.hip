@@ -39,15 +39,17 @@
 #ifndef ULY_NT
 #define ULY_NT 3
 #endif
-// The fused kernel keeps two rows per thread so that they share one
-// divide/sqrt sequence (128 x 2 measured best for it).
+// The generic fused kernel (head dimensions other than 128) keeps two rows
+// per thread so that they share one divide/sqrt sequence (128 x 2 measured
+// best for it).
 #ifndef ULY_FUSED_BLOCK
 #define ULY_FUSED_BLOCK 128
 #endif
 #ifndef ULY_FUSED_UNROLL
 #define ULY_FUSED_UNROLL 2
 #endif
-// 16-byte vectors of one head row per lane in the fused kernel (1, 2 or 4).
+// 16-byte vectors of one head row per lane in the generic fused kernel (1, 2
+// or 4).
 // One is fastest on MI355X: two or four make each load instruction of a
 // wave touch two or four times the cache lines.
 #ifndef ULY_FUSED_VPL
