@@ -72,7 +72,7 @@ def traffic_from_profile():
     return c.get("traffic_bytes_per_launch")
 
 
-def timed(fn, reps, stream, torch, warmup=2):
+def timed(fn, reps, stream, torch, warmup=3):
     """Median and min milliseconds of fn() over reps (after `warmup` untimed
     calls), HIP events on `stream`."""
     for _ in range(warmup):
@@ -328,7 +328,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def time_rows(U, W, torch, dev, stream, reps=10):
+def time_rows(U, W, torch, dev, stream, reps=20):
     """The other hot-path rows, each timed on its own (median of reps)."""
     rows = {}
     h = stream.cuda_stream
