@@ -88,7 +88,7 @@ def timed(fn, reps, stream, torch, warmup=3):
     return statistics.median(ts), min(ts)
 
 
-def cpu_baseline(reps=3, budget_s=30.0):
+def cpu_baseline(reps=5, budget_s=30.0):
     """The oracle as it is (plain index loops, one thread) on the whole
     workload's geometry: one mode 0 and one mode 1 per repetition, median
     rate; stops early once `budget_s` seconds are spent."""
