@@ -59,6 +59,8 @@ def _load():
                                                     _p, _p, ctypes.c_float, _p, _p,
                                                     _i64, _p, _p]
     lib.oracle_qknorm_rope_mode0_sample.restype = ctypes.c_int
+    lib.oracle_row_sum_of_squares.argtypes = [_i64, _p, _p]
+    lib.oracle_row_sum_of_squares.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -190,3 +192,15 @@ def qknorm_rope_mode0_sample(b, d, seq_splits, head_splits, srcs, gamma, eps,
         float(eps), cos_tab.ctypes.data, sin_tab.ctypes.data, rows.shape[0],
         rows.ctypes.data, out.ctypes.data), "qknorm_rope_mode0_sample")
     return out
+
+
+def row_sum_of_squares(d, row_bits):
+    """The fused row operation's fp32 sum of squares of one bf16 row (uint16
+    bit patterns, d elements), in its fixed order."""
+    row = np.ascontiguousarray(np.asarray(row_bits, dtype=np.uint16))
+    if row.shape != (d,):
+        raise ValueError("row must hold d bf16 values")
+    out = np.zeros(1, dtype=np.float32)
+    _check(_load().oracle_row_sum_of_squares(int(d), row.ctypes.data, out.ctypes.data),
+           "row_sum_of_squares")
+    return out[0]

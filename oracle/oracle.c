@@ -21,7 +21,8 @@
  *     page, first two paragraphs);
  *   - QK RMSNorm + RoPE fused into the scatter (0.1.0 "What it does", last
  *     paragraph).  The pages give no formula; the reading written out in
- *     oracle_qknorm_rope_mode0 below is the one this project fixes.
+ *     oracle_qknorm_rope_mode0 below is the one this project fixes, and
+ *     oracle_row_sum_of_squares exposes its first step for the tests.
  *
  * Everything is plain index loops over (rank, batch, sequence, head,
  * element).  The relayout copies raw element bytes and never converts, so
@@ -306,15 +307,13 @@ int oracle_rope_table(double theta, int64_t s_global, int64_t d,
  *        o[2p+1] = y[2p]*sin + y[2p+1]*cos,
  *      each product rounded before the add / subtract;
  *   7. round each o[i] to bf16, nearest-even. */
-static void norm_rope_row(const uint16_t *x, uint16_t *o, int64_t d,
-                          const float *gamma, float eps,
-                          const float *cos_row, const float *sin_row)
+/* Sum of squares of one row in the fixed fp32 order: one fused
+ * multiply-add chain per group of 8 consecutive elements (ascending), then
+ * the pairwise tree over the d/8 partial sums with adjacent pairing. */
+static float row_sum_of_squares(const float *xf, int64_t d)
 {
-    float xf[4096], y[4096], part[512];
-    float ss, ms, inv;
-    int64_t i, l, k, n, p;
-    for (i = 0; i < d; ++i)
-        xf[i] = bf16_to_float(x[i]);
+    float part[512];
+    int64_t i, l, k, n;
     for (l = 0; l < d / 8; ++l) {
         part[l] = 0.0f;
         for (i = 8 * l; i < 8 * l + 8; ++i)
@@ -323,7 +322,19 @@ static void norm_rope_row(const uint16_t *x, uint16_t *o, int64_t d,
     for (n = d / 8; n > 1; n /= 2)
         for (k = 0; k < n / 2; ++k)
             part[k] = part[2 * k] + part[2 * k + 1];
-    ss = part[0];
+    return part[0];
+}
+
+static void norm_rope_row(const uint16_t *x, uint16_t *o, int64_t d,
+                          const float *gamma, float eps,
+                          const float *cos_row, const float *sin_row)
+{
+    float xf[4096], y[4096];
+    float ss, ms, inv;
+    int64_t i, p;
+    for (i = 0; i < d; ++i)
+        xf[i] = bf16_to_float(x[i]);
+    ss = row_sum_of_squares(xf, d);
     ms = ss / (float)d;
     inv = 1.0f / sqrtf(ms + eps);
     for (i = 0; i < d; ++i)
@@ -348,6 +359,21 @@ static int fused_d_ok(int64_t d)
         if (n % 2 != 0)
             return 0; /* the adjacent-pairing tree needs a power of two */
     return 1;
+}
+
+/* The fixed-order sum of squares of one bf16 row of d elements (the first
+ * step of the fused row operation), exposed so that tests can pin the order
+ * on rows whose partial sums round differently under other orders. */
+int oracle_row_sum_of_squares(int64_t d, const uint16_t *x, float *ss)
+{
+    float xf[4096];
+    int64_t i;
+    if (!fused_d_ok(d) || !x || !ss)
+        return -1;
+    for (i = 0; i < d; ++i)
+        xf[i] = bf16_to_float(x[i]);
+    *ss = row_sum_of_squares(xf, d);
+    return 0;
 }
 
 /* Mode-0 relayout of one bf16 tensor (q or k) with RMSNorm over d and RoPE

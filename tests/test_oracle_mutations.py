@@ -45,6 +45,10 @@ MUTANTS = [
      "sin_tab + (S - g.seq_off[j]) * (d / 2));"),
     ("partial sums skip an element", "for (i = 8 * l; i < 8 * l + 8; ++i)",
      "for (i = 8 * l; i < 8 * l + 7; ++i)"),
+    ("one chain over the whole row", "part[l] = fmaf(xf[i], xf[i], part[l]);",
+     "part[0] = fmaf(xf[i], xf[i], part[0]);"),
+    ("tree pairs the halves first", "part[k] = part[2 * k] + part[2 * k + 1];",
+     "part[k] = part[k] + part[k + n / 2];"),
     ("tree drops the odd partial", "part[k] = part[2 * k] + part[2 * k + 1];",
      "part[k] = part[2 * k] + part[2 * k];"),
 ]

@@ -409,6 +409,26 @@ def test_fused_one_hot_closed_form():
     assert np.all(oracle.bf16_to_f32(got[1]) == 0.0)
 
 
+@pytest.mark.parametrize("d", [32, 128])
+def test_sum_of_squares_order(d):
+    """The order of the fp32 sum of squares, pinned by a row whose partial
+    sums round differently under other orders.  Ones at elements 0, 1 (first
+    group of 8: partial 2), 8 (partial 1), 16, 17, 18 (partial 3) and 4096 at
+    element 24 (partial 2^24); every partial is exact.  The adjacent-pairing
+    tree adds (2 + 1) = 3 and (3 + 2^24) = 2^24 + 3, a tie between 2^24 + 2 and
+    2^24 + 4 that goes to the even 2^24 + 4; then 3 + 2^24 + 4 = 2^24 + 7, a
+    tie that goes to the even 2^24 + 8 (zero partials beyond the fourth add
+    nothing).  Pairing the halves first (2 + 3, 1 + 2^24) gives 2^24 + 4, and a
+    single chain over the row gives 2^24 + 6."""
+    row = np.zeros(d, np.float64)
+    row[[0, 1, 8, 16, 17, 18]] = 1.0
+    row[24] = 4096.0
+    ss = oracle.row_sum_of_squares(d, torch_bf16_bits(row))
+    assert ss == np.float32(2 ** 24 + 8)
+    with pytest.raises(ValueError):
+        oracle.row_sum_of_squares(24, np.zeros(24, np.uint16))
+
+
 def test_fused_position_is_global():
     """W ranks give the same rows as one rank holding the whole sequence:
     RoPE uses the global position seq_off_j + s, not the local s."""
