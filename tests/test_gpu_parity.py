@@ -456,6 +456,41 @@ def test_fused_many_heads_full_compare(world, heads):
         assert hist[2] == 0 and hist[3] == 0
 
 
+@pytest.mark.parametrize("d", [32, 128])
+def test_fused_sum_order_reaches_the_output(d):
+    """A row whose fp32 sum of squares depends on the summation order:
+    partial sums 2, 1, 3 and 2^24 give 2^24 + 8 under the fixed
+    adjacent-pairing order (pinned on the CPU), 2^24 + 4 with the halves
+    paired first and 2^24 + 6 in one chain.  Element 0 holds 1 and its gain
+    is chosen so that its bf16 output differs between those three sums (the
+    row sits at position 0, where the rotation is the identity); the GPU's
+    row must equal the oracle's bit for bit."""
+    H.say(f"case: fused summation order d={d}")
+    row = np.zeros(d)
+    row[[0, 1, 8, 16, 17, 18]] = 1.0
+    row[24] = 4096.0
+    g0 = np.float32(1.2512479)
+    f32 = np.float32
+
+    def out0(ss):   # bf16 bits of element 0 for a given sum of squares
+        inv = f32(1) / np.sqrt(f32(f32(ss) / f32(d)) + f32(EPS))
+        return H.to_np(torch.tensor([(f32(1) * inv) * g0], dtype=torch.float32)
+                       .to(torch.bfloat16))[0]
+    assert out0(2 ** 24 + 8) != out0(2 ** 24 + 4) and out0(2 ** 24 + 8) != out0(2 ** 24 + 6)
+    x = torch.tensor(row, dtype=torch.float32).to(torch.bfloat16).reshape(1, 1, 1, d)
+    gamma = np.ones(d, np.float32)
+    gamma[0] = g0
+    plan = U.ulysses_plan_create(1, 1, d, [1], [1], "bf16")
+    qs, ks = [x.to(DEV)], [x.to(DEV)]
+    g = torch.from_numpy(gamma).to(DEV)
+    tab, (oc, osn) = rope_tables(1, d)
+    qo, ko = run_fused(plan, qs, ks, g, g, tab)
+    want = oracle.qknorm_rope_mode0(1, d, [1], [1], [H.to_np(x)], gamma, EPS, oc, osn)[0]
+    assert want.reshape(-1)[0] == out0(2 ** 24 + 8)
+    for o in (qo[0], ko[0]):
+        assert np.array_equal(H.to_np(o), want)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_random_fused(seed):
     rng = np.random.default_rng(4000 + seed)
