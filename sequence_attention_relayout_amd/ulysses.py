@@ -96,23 +96,40 @@ def _dtype_code(dtype):
             "float8_e5m2": 4, "int8": 5, "uint8": 6}[name]
 
 
-def _addr(x):
+ELEM_BYTES = {0: 2, 1: 2, 2: 4, 3: 1, 4: 1, 5: 1, 6: 1}
+
+
+def _nm(what, index):
+    return what if index is None else f"{what}[{index}]"
+
+
+def _addr(x, need=None, what="buffer", index=None):
+    """Device address of x.  A tensor must be contiguous and, when the call
+    reads or writes `need` > 0 bytes through it, hold at least that many
+    bytes on a HIP device: the library takes bare pointers and cannot check
+    either.  Integer addresses are passed through unchecked."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
     if hasattr(x, "data_ptr"):
         if hasattr(x, "is_contiguous") and not x.is_contiguous():
-            raise ValueError("device buffers must be contiguous")
+            raise ValueError(f"{_nm(what, index)}: device buffers must be contiguous")
+        if need and hasattr(x, "nbytes"):
+            if x.nbytes < need:
+                raise ValueError(f"{_nm(what, index)}: holds {x.nbytes} bytes, the call uses {need}")
+            if not getattr(x, "is_cuda", True):
+                raise ValueError(f"{_nm(what, index)}: is on {x.device}, not on a HIP device")
         return x.data_ptr()
-    raise TypeError(f"expected a tensor or an integer address, got {type(x)}")
+    raise TypeError(f"{_nm(what, index)}: expected a tensor or an integer address, got {type(x)}")
 
 
-def _ptr_array(items, world, what):
+def _ptr_array(items, world, what, needs=None):
     items = list(items)
     if len(items) != world:
         raise ValueError(f"{what}: need {world} pointers, got {len(items)}")
-    return (_p * world)(*[_addr(v) for v in items])
+    needs = needs if needs is not None else [None] * world
+    return (_p * world)(*[_addr(v, n, what, i) for i, (v, n) in enumerate(zip(items, needs))])
 
 
 def _stream(stream):
@@ -138,12 +155,23 @@ class Plan:
         self.seq_splits, self.head_splits = list(seq_splits), list(head_splits)
         self.dtype = dtype
         self.window_cap_bytes = window_cap_bytes
+        self._bytes = {}
 
     @property
     def handle(self):
         if self._handle is None:
             raise ValueError("plan was destroyed")
         return self._handle
+
+    def shard_bytes(self, mode, is_dst):
+        """Bytes of each rank's shard: the input (is_dst False) or output of
+        `mode`, as a list over ranks (cached)."""
+        key = (int(mode), bool(is_dst))
+        if key not in self._bytes:
+            esz = ELEM_BYTES[self.dtype]
+            self._bytes[key] = [int(np.prod(ulysses_plan_shape(self, mode, r, is_dst))) * esz
+                                for r in range(self.world)]
+        return self._bytes[key]
 
     def destroy(self):
         if self._handle is not None and _lib is not None:
@@ -191,8 +219,9 @@ def ulysses_plan_bytes(plan, mode):
 
 def ulysses_a2a_4d(plan, mode, src, dst, stream=None):
     w = plan.world
-    _check(_load().ulysses_a2a_4d(plan.handle, int(mode), _ptr_array(src, w, "src"),
-                                  _ptr_array(dst, w, "dst"), _stream(stream)))
+    _check(_load().ulysses_a2a_4d(
+        plan.handle, int(mode), _ptr_array(src, w, "src", plan.shard_bytes(mode, False)),
+        _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)), _stream(stream)))
 
 
 def ulysses_a2a_4d_multi(plan, mode, srcs, dsts, stream=None):
@@ -203,10 +232,11 @@ def ulysses_a2a_4d_multi(plan, mode, srcs, dsts, stream=None):
         raise ValueError("need the same number (>= 1) of source and destination tensors")
     flat_s = [x for t in srcs for x in _check_len(t, w, "src")]
     flat_d = [x for t in dsts for x in _check_len(t, w, "dst")]
-    _check(_load().ulysses_a2a_4d_multi(plan.handle, int(mode), len(srcs),
-                                        _ptr_array(flat_s, len(flat_s), "src"),
-                                        _ptr_array(flat_d, len(flat_d), "dst"),
-                                        _stream(stream)))
+    _check(_load().ulysses_a2a_4d_multi(
+        plan.handle, int(mode), len(srcs),
+        _ptr_array(flat_s, len(flat_s), "src", plan.shard_bytes(mode, False) * len(srcs)),
+        _ptr_array(flat_d, len(flat_d), "dst", plan.shard_bytes(mode, True) * len(dsts)),
+        _stream(stream)))
 
 
 def _check_len(items, world, what):
@@ -217,19 +247,27 @@ def _check_len(items, world, what):
 
 
 def ulysses_a2a_4d_chunked(plan, mode, src, dst, window, stream=None):
+    """window: W device buffers, window r holding one batch plane of
+    destination r (ulysses_plan_window_bytes is enough for every rank)."""
     w = plan.world
-    _check(_load().ulysses_a2a_4d_chunked(plan.handle, int(mode), _ptr_array(src, w, "src"),
-                                          _ptr_array(dst, w, "dst"),
-                                          _ptr_array(window, w, "window"), _stream(stream)))
+    planes = [n // plan.b for n in plan.shard_bytes(mode, True)]
+    _check(_load().ulysses_a2a_4d_chunked(
+        plan.handle, int(mode), _ptr_array(src, w, "src", plan.shard_bytes(mode, False)),
+        _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)),
+        _ptr_array(window, w, "window", planes), _stream(stream)))
 
 
 def ulysses_a2a_4d_qknorm_rope(plan, q_src, q_dst, k_src, k_dst, gamma_q, gamma_k, eps,
                                rope_cos, rope_sin, stream=None):
     w = plan.world
+    sb, db = plan.shard_bytes(0, False), plan.shard_bytes(0, True)
+    gb = 4 * plan.d
+    tb = 4 * sum(plan.seq_splits) * (plan.d // 2)
     _check(_load().ulysses_a2a_4d_qknorm_rope(
-        plan.handle, _ptr_array(q_src, w, "q_src"), _ptr_array(q_dst, w, "q_dst"),
-        _ptr_array(k_src, w, "k_src"), _ptr_array(k_dst, w, "k_dst"), _addr(gamma_q),
-        _addr(gamma_k), float(eps), _addr(rope_cos), _addr(rope_sin), _stream(stream)))
+        plan.handle, _ptr_array(q_src, w, "q_src", sb), _ptr_array(q_dst, w, "q_dst", db),
+        _ptr_array(k_src, w, "k_src", sb), _ptr_array(k_dst, w, "k_dst", db),
+        _addr(gamma_q, gb, "gamma_q"), _addr(gamma_k, gb, "gamma_k"), float(eps),
+        _addr(rope_cos, tb, "rope_cos"), _addr(rope_sin, tb, "rope_sin"), _stream(stream)))
 
 
 def ulysses_rope_table(theta, s_global, d):

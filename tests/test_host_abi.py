@@ -187,6 +187,35 @@ def test_call_errors_before_launch():
            [g, BASE + (15 << 33)], g + 64, g + 128, 1e-6, t, t + (1 << 28), 0)
 
 
+def test_binding_checks_tensor_size_and_device():
+    """The C ABI takes bare pointers; the Python binding checks what a
+    tensor argument can tell it before any pointer is passed: enough bytes
+    for the shard the call touches, contiguity, and a HIP device (a host
+    tensor's address would fault the GPU).  Host tensors only here, so every
+    call fails before reaching the library."""
+    import torch
+    plan = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16", 1 << 20)
+    assert plan.shard_bytes(0, False) == [3 * 3 * 8 * 2, 4 * 3 * 8 * 2]
+    assert plan.shard_bytes(0, True) == [7 * 1 * 8 * 2, 7 * 2 * 8 * 2]
+    xs = [torch.zeros(U.ulysses_plan_shape(plan, 0, r, False), dtype=torch.bfloat16)
+          for r in range(2)]
+    ys = [torch.zeros(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16)
+          for r in range(2)]
+    with pytest.raises(ValueError, match=r"src\[0\]: is on cpu"):
+        U.ulysses_a2a_4d(plan, 0, xs, ys, 0)
+    with pytest.raises(ValueError, match=r"src\[0\]: holds 48 bytes, the call uses 144"):
+        U.ulysses_a2a_4d(plan, 0, [xs[0][:, :1], xs[1]], ys, 0)
+    with pytest.raises(ValueError, match=r"dst\[1\]: device buffers must be contiguous"):
+        U.ulysses_a2a_4d(plan, 0, fake(2), [fake(1)[0], ys[1].transpose(1, 2)], 0)
+    with pytest.raises(ValueError, match=r"window\[0\]: holds 2 bytes"):
+        U.ulysses_a2a_4d_chunked(plan, 0, fake(2), fake(2, off=1 << 36),
+                                 [torch.zeros(1, dtype=torch.bfloat16), fake(1)[0]], 0)
+    with pytest.raises(ValueError, match=r"rope_cos: holds 4 bytes"):
+        U.ulysses_a2a_4d_qknorm_rope(plan, fake(2), fake(2, off=1 << 36), fake(2, off=1 << 37),
+                                     fake(2, off=3 << 36), BASE, BASE + 64, 1e-6,
+                                     torch.zeros(1), BASE + 128, 0)
+
+
 def test_launch_wider_than_grid_x_refused():
     """8 shards of 2^30 16-byte vectors per plane: one pass needs more than
     2^32 threads along x, which one launch cannot hold; the call refuses
