@@ -47,4 +47,11 @@ def all_to_all_4d(plan, xs, mode=0):
     differentiable with respect to the inputs."""
     if len(xs) != plan.world:
         raise ValueError(f"need {plan.world} shards, got {len(xs)}")
+    esz = U.ELEM_BYTES[plan.dtype]
+    for r, x in enumerate(xs):
+        if x.element_size() != esz:
+            raise ValueError(f"shard {r}: {x.dtype} does not have the plan's {esz}-byte elements")
+        if tuple(x.shape) != U.ulysses_plan_shape(plan, mode, r, False):
+            raise ValueError(f"shard {r}: shape {tuple(x.shape)}, the plan's is "
+                             f"{U.ulysses_plan_shape(plan, mode, r, False)}")
     return list(_AllToAll4D.apply(plan, int(mode), *xs))

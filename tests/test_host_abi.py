@@ -216,6 +216,18 @@ def test_binding_checks_tensor_size_and_device():
                                      torch.zeros(1), BASE + 128, 0)
 
 
+def test_autograd_entry_checks_dtype_and_shape():
+    import torch
+    from sequence_attention_relayout_amd.autograd import all_to_all_4d
+    plan = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16")
+    good = [torch.zeros(U.ulysses_plan_shape(plan, 0, r, False), dtype=torch.bfloat16)
+            for r in range(2)]
+    with pytest.raises(ValueError, match="2-byte elements"):
+        all_to_all_4d(plan, [good[0].float(), good[1]], 0)
+    with pytest.raises(ValueError, match="shape"):
+        all_to_all_4d(plan, [good[1], good[0]], 0)
+
+
 def test_launch_wider_than_grid_x_refused():
     """8 shards of 2^30 16-byte vectors per plane: one pass needs more than
     2^32 threads along x, which one launch cannot hold; the call refuses
