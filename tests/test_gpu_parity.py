@@ -150,6 +150,54 @@ def test_random_geometries_every_dtype(seed):
         check_full(mode, b, d, seq, head, xs, outs)
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_random_medium_geometries(seed):
+    """Larger random geometries (up to ~48 MB per tensor): many bands per
+    piece, long and short rows, uneven and zero splits, every dtype; every
+    element compared in both modes, plus the fused path for bf16 with
+    d = 128 (band kernel) or another d (generic kernel)."""
+    rng = np.random.default_rng(7000 + seed)
+    dt = W.DTYPES[seed % len(W.DTYPES)]
+    esz = W.ELEM_BYTES[dt]
+    world = int(rng.integers(1, 9))
+    b = int(rng.integers(1, 4))
+    d = (16 // esz) * int(rng.choice([1, 2, 4, 8, 16]))
+    head = [int(v) for v in rng.integers(0, 9, world)]
+    head[-1] = max(head[-1], 1)
+    row = sum(head) * d * esz
+    per_rank = max(1, (48 << 20) // (b * row * world))
+    seq = [int(v) for v in rng.integers(0, per_rank + 1, world)]
+    if seed % 4 == 1 and world > 1:
+        seq[int(rng.integers(0, world))] = 0
+    seq[0] = max(seq[0], 1)
+    H.say(f"case: random medium seed={seed} dtype={dt} W={world} b={b} d={d} "
+          f"seq={seq} head={head}")
+    plan = U.ulysses_plan_create(world, b, d, seq, head, dt)
+    wl = W.Workload("random medium", world, b, d, seq, head)
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, dt, 7100 + seed * 2 + mode, DEV)
+        check_full(mode, b, d, seq, head, xs, run_relayout(plan, mode, xs, dt).views)
+    if dt != "bf16":
+        return
+    fd = [128, 64, 256][seed % 3]
+    fseq = [max(1, v // 8) for v in seq]
+    fplan = U.ulysses_plan_create(world, b, fd, fseq, head, "bf16")
+    fwl = W.Workload("random medium fused", world, b, fd, fseq, head)
+    qs = W.make_shards(fwl, 0, "bf16", 7200 + seed, DEV)
+    ks = W.make_shards(fwl, 0, "bf16", 7300 + seed, DEV)
+    gq, gk = W.make_gamma(fd, 7400 + seed, DEV), W.make_gamma(fd, 7500 + seed, DEV)
+    tab, (oc, osn) = rope_tables(sum(fseq), fd)
+    qo, ko = run_fused(fplan, qs, ks, gq, gk, tab)
+    for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
+        want = oracle.qknorm_rope_mode0(b, fd, fseq, head, [H.to_np(x) for x in src],
+                                        g.cpu().numpy(), EPS, oc, osn)
+        hist = np.zeros(4, np.int64)
+        for o, w in zip(out, want):
+            hist += ulp_hist(H.to_np(o), w)
+        H.say(f"  fused d={fd} ulp histogram (0,1,2,>=3): {hist.tolist()}")
+        assert hist[2] == 0 and hist[3] == 0
+
+
 # ---------------------------------------------------------------------------
 # the W=8, 75,600-token video-DiT operand (the timed workload)
 # ---------------------------------------------------------------------------
