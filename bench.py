@@ -165,7 +165,7 @@ def main():
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world_env != 1:
         print("bench.py measures one GPU: the W ranks are emulated as shard buffers in one "
-              "GPU's HBM, and this build has no multi-GPU path. Run with --gpus 1.",
+              "GPU's HBM, and the library has no multi-GPU path. Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

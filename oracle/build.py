@@ -1,7 +1,7 @@
 """Compile the CPU oracle into oracle/liboracle.so (gcc, no fast-math).
 
 Test infrastructure: only the tests, the smoke check and the benchmark's
-CPU-baseline leg use the library this builds.
+CPU-baseline leg use liboracle.so.
 """
 import os
 import subprocess
