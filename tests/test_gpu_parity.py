@@ -606,6 +606,78 @@ def test_w8_fused_full_size():
 # edge cases
 # ---------------------------------------------------------------------------
 
+def gather_device(outs, coords):
+    """Values of device shards at coords (n x 5), gathered on the device."""
+    got = np.empty(len(coords), dtype=H.to_np(outs[0][:0]).dtype)
+    for r, o in enumerate(outs):
+        sel = coords[:, 0] == r
+        if sel.any():
+            idx = [torch.from_numpy(coords[sel, i]).to(DEV) for i in range(1, 5)]
+            got[sel] = H.to_np(o[idx[0], idx[1], idx[2], idx[3]])
+    return got
+
+
+def test_shards_beyond_4_gib():
+    """Shards of 4.5-4.9 GB: byte offsets past 2^32 inside one shard, for both
+    modes of the relayout and for the fused band kernel (d = 128), whose lane
+    offsets are 32-bit on 64-bit block bases.  Sampled elements and rows,
+    including the last rows of every shard, against the oracle."""
+    seq, head, d = [2_200_000, 2_300_000], [4, 4], 256
+    H.say(f"case: relayout uint8 W=2 seq={seq} head={head} d={d} (shards > 4 GiB)")
+    plan = U.ulysses_plan_create(2, 1, d, seq, head, "uint8")
+    wl = W.Workload("beyond 4 GiB", 2, 1, d, seq, head)
+    rng = np.random.default_rng(90)
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, "uint8", 91 + mode, DEV)
+        assert max(x.numel() for x in xs) > (1 << 32)
+        ys = [torch.empty(s_, dtype=torch.uint8, device=DEV) for s_ in dst_shapes(plan, mode)]
+        U.ulysses_a2a_4d(plan, mode, xs, ys)
+        torch.cuda.synchronize()
+        rows = boundary_rows(mode, 1, seq, head)
+        rows += [(r, 0, y.shape[1] - 1 - i) for r, y in enumerate(ys) for i in range(3)]
+        coords = H.sample_coords(rng, [tuple(y.shape) for y in ys], 200_000, rows)
+        host = [H.to_np(x) for x in xs]
+        want = oracle.a2a_4d_sample(mode, 1, d, seq, head, host, coords)
+        bad = np.count_nonzero(gather_device(ys, coords) != want)
+        H.say(f"  mode {mode}: {len(coords)} sampled elements, {bad} differ")
+        assert bad == 0
+        del xs, ys, host
+        torch.cuda.empty_cache()
+
+    seq, head = [1_100_000, 1_200_000], [8, 8]
+    H.say(f"case: fused d=128 W=2 seq={seq} head={head} (shards > 4 GiB)")
+    plan = U.ulysses_plan_create(2, 1, 128, seq, head, "bf16")
+    wl = W.Workload("fused beyond 4 GiB", 2, 1, 128, seq, head)
+    qs = W.make_shards(wl, 0, "bf16", 93, DEV)
+    ks = W.make_shards(wl, 0, "bf16", 94, DEV)
+    assert max(x.numel() * 2 for x in qs) > (1 << 32)
+    gq, gk = W.make_gamma(128, 95, DEV), W.make_gamma(128, 96, DEV)
+    c, s = U.ulysses_rope_table(THETA, sum(seq), 128)
+    tc, ts = torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV)
+    qo = [torch.empty(s_, dtype=torch.bfloat16, device=DEV) for s_ in dst_shapes(plan, 0)]
+    ko = [torch.empty_like(t) for t in qo]
+    U.ulysses_a2a_4d_qknorm_rope(plan, qs, qo, ks, ko, gq, gk, EPS, tc, ts)
+    torch.cuda.synchronize()
+    s_global = sum(seq)
+    picks = {int(v) for v in rng.integers(0, s_global, 1500)}
+    picks |= {0, seq[0] - 1, seq[0], s_global - 2, s_global - 1}
+    rows = np.array([(r, 0, S, h) for r in range(2) for S in sorted(picks)
+                     for h in range(head[r])], dtype=np.int64)
+    host = [H.to_np(x) for x in qs]
+    want = oracle.qknorm_rope_mode0_sample(1, 128, seq, head, host, gq.cpu().numpy(), EPS,
+                                           c, s, rows)
+    got = np.empty_like(want)
+    for r in range(2):
+        sel = rows[:, 0] == r
+        idx = torch.from_numpy(rows[sel, 2]).to(DEV), torch.from_numpy(rows[sel, 3]).to(DEV)
+        got[sel] = H.to_np(qo[r][0][idx[0], idx[1]])
+    hist = ulp_hist(got, want)
+    H.say(f"  q: {len(rows)} rows, ulp histogram (0,1,2,>=3): {hist.tolist()}")
+    assert hist[2] == 0 and hist[3] == 0
+    del qs, ks, qo, ko, host
+    torch.cuda.empty_cache()
+
+
 def test_world_one_is_a_copy():
     H.say("case: W=1 identity, b=3")
     plan = U.ulysses_plan_create(1, 3, 64, [333], [7], "fp16")
