@@ -369,11 +369,34 @@ def time_rows(U, W, torch, dev, stream, reps=20):
         tiny_step()
     torch.cuda.synchronize()
     host_us = (time.perf_counter() - t0) / 1000 * 1e6
+    # the same two launches captured once in a HIP graph and replayed: the
+    # device-side floor without the per-call host path
+    def tiny_step_current_stream():
+        U.ulysses_a2a_4d(plan, 0, xs, ys)
+        U.ulysses_a2a_4d(plan, 1, ys, zs)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        tiny_step_current_stream()          # warm-up on the capture stream
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        tiny_step_current_stream()
+    for z in zs:
+        z.zero_()
+    med_graph, _ = timed(graph.replay, 50, stream, torch)
+    torch.cuda.synchronize()
+    roundtrip = all(torch.equal(x.view(torch.int16), z.view(torch.int16)) for x, z in zip(xs, zs))
     rows["w2_tiny_latency"] = {"step_median_us": round(med_tiny * 1e3, 2),
                                "host_us_per_call": round(host_us, 2),
+                               "graph_replay_step_median_us": round(med_graph * 1e3, 2),
+                               "graph_replay_roundtrip_exact": roundtrip,
                                "note": "mode 0 + mode 1 of the two-rank example (65,536 B "
-                                       "per mode); host time per ABI call through Python"}
-    del xs, ys, zs
+                                       "per mode); host time per ABI call through Python; the "
+                                       "same two launches replayed from one captured HIP graph"}
+    del graph, xs, ys, zs
 
     # q, k and v of the timed geometry: one launch against three
     wl = wls["w8_wan720p"]
