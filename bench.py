@@ -348,6 +348,23 @@ def time_rows(U, W, torch, dev, stream, reps=20):
                 "bytes": nb}
             del xs, ys
         torch.cuda.empty_cache()
+
+    # unequal head widths (6 and 4 heads per rank): the row-aligned walk
+    world, heads = 8, [6, 6, 6, 6, 4, 4, 4, 4]
+    seq = W.even_splits(75600, world)
+    plan = U.ulysses_plan_create(world, 1, 128, seq, heads, "bf16")
+    wlu = W.Workload("w8 unequal heads", world, 1, 128, seq, heads)
+    for mode in (0, 1):
+        xs = W.make_shards(wlu, mode, "bf16", 45 + mode, dev)
+        ys = [torch.empty(U.ulysses_plan_shape(plan, mode, r, True), dtype=torch.bfloat16,
+                          device=dev) for r in range(world)]
+        med, _ = timed(lambda: U.ulysses_a2a_4d(plan, mode, xs, ys, h), reps, stream, torch)
+        nb = U.ulysses_plan_bytes(plan, mode)
+        rows[f"w8_heads_6x4_4x4_mode{mode}"] = {
+            "gbs": round(nb / (med * 1e-3) / 1e9, 1), "median_us": round(med * 1e3, 1),
+            "bytes": nb}
+        del xs, ys
+    torch.cuda.empty_cache()
     log("uneven rows done")
 
     # the two-rank example: launch-bound, so this is latency, not bandwidth

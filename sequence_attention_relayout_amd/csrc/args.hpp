@@ -86,6 +86,19 @@ struct RelayoutArgs {
     uint32_t world;
     uint32_t band_rows;
     uint32_t band_vecs;
+    // Row-aligned chunk traversal (fill_relayout_aligned; band_vecs == 0 and
+    // chunks_per_band != 0), for groups whose pieces have unequal row widths:
+    // a band is band_rows rows of every piece of the group, cut into chunks
+    // of chunk_vecs vectors (a whole number per piece);
+    // block grp_begin[g] + band * chunks_per_band + q takes chunk
+    // q - chunk_begin[k] of piece (g, k), k being the last piece with
+    // chunk_begin[k] <= q.  band_m/band_s1/band_s2 divide exactly by
+    // chunks_per_band (div32).
+    uint32_t chunk_begin[kMaxWorld + 1];
+    uint32_t chunks_per_band;
+    uint32_t chunk_vecs;
+    uint32_t band_m;
+    uint32_t band_s1, band_s2;
 };
 
 // The fused QK-norm + RoPE mode-0 pass: the same piece table for q and k

@@ -151,12 +151,31 @@ __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs
 #pragma unroll
     for (int q = 1; q < kMaxWorld; ++q) g += (a.grp_begin[q] <= x) ? 1u : 0u;
     const uint32_t local = x - a.grp_begin[g];
-    const uint32_t band = local / a.world;
-    const uint32_t k = local - band * a.world;
+    uint32_t k, begin, end;
+    if (a.chunks_per_band != 0) {
+        // row-aligned chunks: band of band_rows rows of every piece, chunk c
+        // of piece k (chunk_begin is non-decreasing; the last entry <= q
+        // always belongs to a piece with chunks)
+        const uint32_t band = div32(local, a.band_m, a.band_s1, a.band_s2);
+        const uint32_t q = local - band * a.chunks_per_band;
+        k = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxWorld; ++i) k += (a.chunk_begin[i] <= q) ? 1u : 0u;
+        const uint32_t c = q - a.chunk_begin[k];
+        const uint32_t vpr = a.piece[g * a.world + k].vpr;
+        const uint32_t band0 = band * a.band_rows * vpr;
+        begin = band0 + c * a.chunk_vecs;
+        end = min(min(begin + a.chunk_vecs, band0 + a.band_rows * vpr),
+                  a.piece[g * a.world + k].nvec);
+    } else {
+        const uint32_t band = local / a.world;
+        k = local - band * a.world;
+        const uint32_t vpr = a.piece[g * a.world + k].vpr;
+        const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * vpr;
+        begin = band * span;
+        end = min(begin + span, a.piece[g * a.world + k].nvec);
+    }
     const PieceArgs pc = a.piece[g * a.world + k];
-    const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * pc.vpr;
-    const uint32_t begin = band * span;
-    const uint32_t end = min(begin + span, pc.nvec);
     const uint64_t ps = uint64_t(a.src_plane0) + blockIdx.y;
     const uint64_t pd = uint64_t(a.dst_plane0) + blockIdx.y;
     const unsigned char *sb = a.src[blockIdx.z][pc.j] + (ps * a.src_plane[pc.j] + pc.src_off) * 16;

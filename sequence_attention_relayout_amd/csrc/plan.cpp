@@ -253,6 +253,64 @@ uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
     return blocks;
 }
 
+uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_rows,
+                               RelayoutArgs *a) {
+    const ModeGeom &g = p.mode[mode];
+    // Row widths of the k-th piece of a group: the same for every group
+    // (mode 0: destination r = k; mode 1: source j = k).
+    uint32_t vpr[kMaxWorld] = {};
+    uint32_t common = 0;   // gcd of the non-zero widths
+    uint32_t first = 0;
+    bool uneven = false;
+    for (int k = 0; k < p.world; ++k) {
+        vpr[k] = static_cast<uint32_t>(p.R[k] / 16);
+        if (vpr[k] == 0) continue;
+        if (first == 0) first = vpr[k];
+        else if (vpr[k] != first) uneven = true;
+        uint32_t x = common, y = vpr[k];
+        while (y != 0) { const uint32_t t = x % y; x = y; y = t; }
+        common = x;
+    }
+    if (!uneven || chunk_vecs == 0) return 0;
+    uint32_t gc = common, y = chunk_vecs;   // gcd(chunk_vecs, common)
+    while (y != 0) { const uint32_t t = gc % y; gc = y; y = t; }
+    // R * vpr_k is a multiple of chunk_vecs for R = chunk_vecs / gc
+    const uint32_t rows_per_band = chunk_vecs / gc;
+    if (max_rows != 0 && rows_per_band > max_rows) return 0;
+    clear_table(a);
+    for (int r = 0; r < p.world; ++r) {
+        a->src_plane[r] = static_cast<uint64_t>(g.src_plane[r] / 16);
+        a->dst_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
+    }
+    a->world = static_cast<uint32_t>(p.world);
+    a->band_rows = rows_per_band;
+    a->chunk_vecs = chunk_vecs;
+    uint32_t n = 0;
+    for (int k = 0; k < p.world; ++k) {
+        a->chunk_begin[k] = n;
+        n += static_cast<uint32_t>(uint64_t(rows_per_band) * vpr[k] / chunk_vecs);
+    }
+    for (int k = p.world; k <= kMaxWorld; ++k) a->chunk_begin[k] = n;
+    a->chunks_per_band = n;
+    const Div32Magic dm = div32_magic(n);
+    a->band_m = dm.m;
+    a->band_s1 = dm.s1;
+    a->band_s2 = dm.s2;
+    uint64_t blocks = 0;
+    for (int grp = 0; grp < p.world; ++grp) {
+        const int64_t rows = p.S[grp];
+        const int64_t bands = (rows + rows_per_band - 1) / rows_per_band;
+        for (int k = 0; k < p.world; ++k) {
+            const int j = mode == 0 ? grp : k;
+            const int r = mode == 0 ? k : grp;
+            fill_piece_args(g.piece[j * p.world + r], &a->piece[grp * p.world + k]);
+        }
+        a->grp_begin[grp] = static_cast<uint32_t>(blocks);
+        blocks += static_cast<uint64_t>(bands) * n;
+    }
+    return blocks;
+}
+
 bool to_units(RelayoutArgs *a, uint32_t vpl) {
     if (vpl == 0 || a->band_vecs % vpl) return false;
     a->band_vecs /= vpl;

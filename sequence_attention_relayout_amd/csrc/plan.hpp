@@ -89,6 +89,16 @@ uint64_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, Relayo
 // interleaved over the group as for row bands.  Returns grid.x.
 uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
 
+// Row-aligned chunk table (see RelayoutArgs::chunk_begin) when the pieces of
+// a group differ in row width: bands of R rows, R the fewest rows that make
+// every piece's band a whole number of chunk_vecs-vector chunks, one chunk
+// per block, so blocks running side by side cover the same rows of every
+// piece.  Returns grid.x, or 0 without touching *a when the pieces of a group
+// all have the same width, or when max_rows != 0 and R exceeds it (then
+// fill_relayout_vbands applies).
+uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_rows,
+                               RelayoutArgs *a);
+
 // Band height so that one band of the widest piece moves about
 // `target_vectors` 16-byte vectors (at least one row).
 uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);

@@ -27,6 +27,7 @@
 using namespace ulysses;
 
 static long g_checks = 0;
+static long g_aligned = 0;   // geometries that took the row-aligned table
 
 #define REQUIRE(c, ...)                                              \
     do {                                                             \
@@ -88,12 +89,30 @@ static bool replay_band(const RelayoutArgs &a, uint32_t chunk, uint32_t x, uint3
     uint32_t g = 0;
     for (int q = 1; q < kMaxWorld; ++q) g += a.grp_begin[q] <= x ? 1u : 0u;
     const uint32_t local = x - a.grp_begin[g];
-    const uint32_t band = local / a.world;
-    const uint32_t k = local - band * a.world;
+    uint32_t k, begin, end;
+    if (a.chunks_per_band != 0) {   // row-aligned chunks, as the kernel decodes them
+        const uint32_t band = div32(local, a.band_m, a.band_s1, a.band_s2);
+        REQUIRE(band == local / a.chunks_per_band, "aligned band division");
+        const uint32_t q = local - band * a.chunks_per_band;
+        k = 0;
+        for (int i = 1; i < kMaxWorld; ++i) k += a.chunk_begin[i] <= q ? 1u : 0u;
+        REQUIRE(k < a.world && a.chunk_begin[k + 1] > q, "aligned chunk lands in a piece");
+        const uint32_t c = q - a.chunk_begin[k];
+        const uint32_t vpr = a.piece[g * a.world + k].vpr;
+        const uint32_t band0 = band * a.band_rows * vpr;
+        begin = band0 + c * a.chunk_vecs;
+        REQUIRE(c * a.chunk_vecs < a.band_rows * vpr, "chunk past its band");
+        end = std::min(std::min(begin + a.chunk_vecs, band0 + a.band_rows * vpr),
+                       a.piece[g * a.world + k].nvec);
+    } else {
+        const uint32_t band = local / a.world;
+        k = local - band * a.world;
+        const uint32_t vpr = a.piece[g * a.world + k].vpr;
+        const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * vpr;
+        begin = band * span;
+        end = std::min(begin + span, a.piece[g * a.world + k].nvec);
+    }
     const PieceArgs &pc = a.piece[g * a.world + k];
-    const uint32_t span = a.band_vecs != 0 ? a.band_vecs : a.band_rows * pc.vpr;
-    const uint32_t begin = band * span;
-    const uint32_t end = std::min(begin + span, pc.nvec);
     const uint32_t s0 = begin + c * chunk;
     if (s0 >= end) return false;
     const uint32_t row0 = s0 / pc.vpr;
@@ -144,14 +163,21 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
     const int64_t hv = hb / 16;   // vectors per head row
     for (int mode = 0; mode < 2; ++mode) {
         // traversals 0, 1: flat in both piece orders; 2, 3: row bands of
-        // two heights, with chunks of vpb vectors; 4: bands of vpb vectors
-        for (int trav = 0; trav < 5; ++trav) {
+        // two heights, with chunks of vpb vectors; 4: bands of vpb vectors;
+        // 5: row-aligned chunks (pieces of unequal width only)
+        for (int trav = 0; trav < 6; ++trav) {
             RelayoutArgs a;
             uint32_t gx, nchunks = 1;
             if (trav < 2) {
                 gx = fill_relayout(p, mode, vpb, static_cast<PieceOrder>(trav), &a);
             } else if (trav == 4) {
                 gx = fill_relayout_vbands(p, mode, vpb, &a);
+            } else if (trav == 5) {
+                gx = fill_relayout_aligned(p, mode, vpb, 0, &a);
+                if (gx == 0) continue;   // equal widths: the vector bands apply
+                for (int q = 0; q < p.world; ++q)
+                    REQUIRE(a.band_rows * a.piece[q].vpr % vpb == 0, "aligned band not whole chunks");
+                ++g_aligned;
             } else {
                 const uint32_t rows = trav == 2 ? band_rows_for(p, mode, vpb) : 3;
                 gx = fill_relayout_bands(p, mode, rows, &a);
@@ -398,6 +424,39 @@ static void check_div32(std::mt19937_64 &rng) {
     }
 }
 
+// When the row-aligned table applies: pieces of unequal width whose
+// whole-chunk bands need at most max_rows rows.
+static void check_aligned_choice() {
+    struct Case { std::vector<int64_t> H; uint32_t max_rows; uint32_t rows; };
+    const Case cases[] = {
+        {{6, 6, 6, 6, 4, 4, 4, 4}, 2, 2},   // widths 96/64 vectors: bands of 2 rows
+        {{4, 4, 4, 4, 2, 2, 2, 2}, 2, 2},   // 64/32
+        {{8, 8, 4, 4}, 2, 1},               // 128/64: one row
+        {{6, 6, 6, 6, 5, 5, 5, 5}, 2, 0},   // 96/80 would need 4 rows: vector bands
+        {{6, 6, 6, 6, 5, 5, 5, 5}, 0, 4},   // ... unless uncapped
+        {{5, 5, 5, 5}, 2, 0},               // equal widths: vector bands
+        {{5, 0, 5, 5}, 2, 0},               // an empty piece does not count
+    };
+    for (const Case &c : cases) {
+        const int world = static_cast<int>(c.H.size());
+        std::vector<int64_t> S(world, 7);
+        Plan p;
+        std::string msg;
+        REQUIRE(plan_build(&p, world, 1, 128, S.data(), c.H.data(), 0, 0, &msg) == kOk, "plan");
+        for (int mode = 0; mode < 2; ++mode) {
+            RelayoutArgs a;
+            std::memset(&a, 0x5A, sizeof a);
+            const uint64_t gx = fill_relayout_aligned(p, mode, 64, c.max_rows, &a);
+            if (c.rows == 0) {
+                REQUIRE(gx == 0, "aligned table where vector bands apply");
+            } else {
+                REQUIRE(gx != 0 && a.band_rows == c.rows, "aligned band of %u rows, want %u",
+                        a.band_rows, c.rows);
+            }
+        }
+    }
+}
+
 static void check_errors() {
     Plan p;
     std::string m;
@@ -424,6 +483,7 @@ static void check_errors() {
 int main() {
     check_magic();
     check_errors();
+    check_aligned_choice();
     std::mt19937_64 rng(12345);
     const uint32_t vpbs[] = {64, 256, 1024, 2048};
     const int dtypes[] = {0, 2, 3, 5};
@@ -478,6 +538,7 @@ int main() {
     check_fused_band(8, 1, std::vector<int64_t>(8, 40), std::vector<int64_t>(8, 5), 1);
     check_fused_band(7, 2, {9, 40, 3, 17, 0, 22, 31}, {6, 6, 6, 6, 6, 5, 5}, 2);
     check_div32(rng);
+    REQUIRE(g_aligned > 50, "too few geometries exercised the row-aligned table: %ld", g_aligned);
     std::printf("OK %ld\n", g_checks);
     return 0;
 }

@@ -150,6 +150,23 @@ def test_random_geometries_every_dtype(seed):
         check_full(mode, b, d, seq, head, xs, outs)
 
 
+@pytest.mark.parametrize("head", [[6, 6, 6, 6, 4, 4, 4, 4], [4, 4, 4, 4, 2, 2, 2, 2],
+                                  [8, 8, 4, 4], [4, 2, 0, 2, 6]])
+def test_unequal_head_widths_row_aligned(head):
+    """Head splits whose rows differ in width and make bands of whole chunks
+    within two rows: the relayout walks row-aligned chunks (one band of every
+    piece covers the same rows).  Uneven sequence splits, two batch planes,
+    every element compared in both modes."""
+    world = len(head)
+    seq = W.seeded_partition(11, 2001 * world, world)
+    H.say(f"case: unequal head widths W={world} seq={seq} head={head}")
+    plan = U.ulysses_plan_create(world, 2, 128, seq, head, "bf16")
+    wl = W.Workload("unequal widths", world, 2, 128, seq, head)
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, "bf16", 7700 + mode, DEV)
+        check_full(mode, 2, 128, seq, head, xs, run_relayout(plan, mode, xs, "bf16").views)
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_medium_geometries(seed):
     """Larger random geometries (up to ~48 MB per tensor): many bands per
