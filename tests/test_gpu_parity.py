@@ -150,6 +150,65 @@ def test_random_geometries_every_dtype(seed):
         check_full(mode, b, d, seq, head, xs, outs)
 
 
+def test_many_tiny_random_geometries():
+    """300 tiny random geometries in one process (W 1-8, splits 0-40 with
+    zeros, head counts 0-12, b 1-3, every dtype and several row widths; a
+    third of them with head counts in multiples of 4 so that unequal widths
+    take the row-aligned walk): both modes, the plane-at-a-time call, and
+    the fused call for bf16, every element against the oracle."""
+    rng = np.random.default_rng(9000)
+    aligned = 0
+    for case in range(300):
+        dt = W.DTYPES[int(rng.integers(0, len(W.DTYPES)))]
+        esz = W.ELEM_BYTES[dt]
+        world = int(rng.integers(1, 9))
+        b = int(rng.integers(1, 4))
+        d = (16 // esz) * int(rng.choice([1, 2, 4, 8]))
+        seq = [int(v) for v in rng.integers(0, 41, world)]
+        head = [int(v) for v in rng.integers(0, 10, world)]
+        if case % 3 == 0:   # widths of whole multiples of 32 vectors: row-aligned bands
+            d = (16 // esz) * 8
+            head = [4 * int(v) for v in rng.integers(0, 4, world)]
+        seq[int(rng.integers(0, world))] += 1
+        if sum(head) == 0:
+            head[int(rng.integers(0, world))] += 4
+        widths = {h * d * esz // 16 for h in head if h}
+        g = int(np.gcd.reduce(list(widths)))
+        aligned += len(widths) > 1 and 64 // int(np.gcd(64, g)) <= 2
+        plan = U.ulysses_plan_create(world, b, d, seq, head, dt, 1 << 30)
+        wl = W.Workload("tiny random", world, b, d, seq, head)
+        for mode in (0, 1):
+            xs = W.make_shards(wl, mode, dt, 9100 + 2 * case + mode, DEV)
+            outs = run_relayout(plan, mode, xs, dt).views
+            try:
+                check_full(mode, b, d, seq, head, xs, outs)
+            except AssertionError:
+                H.say(f"failing case {case}: {dt} W={world} b={b} d={d} seq={seq} head={head}")
+                raise
+            if mode == 1:
+                win = [torch.empty(max(1, U.ulysses_plan_window_bytes(plan, 1)), dtype=torch.uint8,
+                                   device=DEV) for _ in range(world)]
+                cout = [torch.empty(s_, dtype=W.torch_dtype(dt), device=DEV)
+                        for s_ in dst_shapes(plan, 1)]
+                U.ulysses_a2a_4d_chunked(plan, 1, xs, cout, win)
+                torch.cuda.synchronize()
+                check_full(1, b, d, seq, head, xs, cout)
+        if dt == "bf16" and (d // 8) & (d // 8 - 1) == 0:
+            qs = W.make_shards(wl, 0, "bf16", 9700 + case, DEV)
+            ks = W.make_shards(wl, 0, "bf16", 9800 + case, DEV)
+            gq, gk = W.make_gamma(d, 9900 + case, DEV), W.make_gamma(d, 9950 + case, DEV)
+            tab, (oc, osn) = rope_tables(sum(seq), d)
+            qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
+            for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
+                want = oracle.qknorm_rope_mode0(b, d, seq, head, [H.to_np(x) for x in src],
+                                                g.cpu().numpy(), EPS, oc, osn)
+                for o, w in zip(out, want):
+                    hist = ulp_hist(H.to_np(o), w)
+                    assert hist[2] == 0 and hist[3] == 0, f"fused case {case}"
+    H.say(f"  300 cases, {aligned} walked in row-aligned chunks")
+    assert aligned > 30
+
+
 @pytest.mark.parametrize("head", [[6, 6, 6, 6, 4, 4, 4, 4], [4, 4, 4, 4, 2, 2, 2, 2],
                                   [8, 8, 4, 4], [4, 2, 0, 2, 6]])
 def test_unequal_head_widths_row_aligned(head):
