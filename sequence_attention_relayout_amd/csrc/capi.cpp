@@ -40,18 +40,19 @@ static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrde
 #define ULY_VBAND 64
 #endif
 
-// Row-aligned chunk bands for groups whose pieces differ in width, used
-// when a band of whole chunks needs at most ULY_ALIGNED_MAX_ROWS rows.  By
-// measurement on MI355X (W=8, 75,600 tokens, d=128, bf16, GB/s per mode):
-// widths 64/32, 96/64 and 128/96 vectors (bands of 1-2 rows) gain 4-21%
-// over vector bands, whose bands drift apart in rows; bands of 4 rows
-// (80/64, 96/80, 80/48, 224/208) gain up to 7% in mode 1 but lose up to 6%
-// in mode 0.
+// Row-aligned chunk bands for groups whose pieces differ in width, used when
+// no piece's band holds more than ULY_ALIGNED_MAX_CHUNKS chunks of 64
+// vectors (one chunk per block, piece by piece within a band).  By
+// measurement on MI355X (W=8 or 7, 75,600 tokens, d=128, GB/s per mode):
+// bands of 1-4 chunks per piece gain 5-21% over vector bands, whose bands
+// drift apart in rows (bf16 widths 64/32, 96/64, 128/96; fp32 192/128,
+// 256/192); runs of 5-7 chunks per piece gain up to 7% in mode 1 but lose up
+// to 6% in mode 0 (bf16 80/64, 96/80, 80/48, 224/160; fp32 192/160).
 #ifndef ULY_ALIGNED
 #define ULY_ALIGNED 1
 #endif
-#ifndef ULY_ALIGNED_MAX_ROWS
-#define ULY_ALIGNED_MAX_ROWS 2
+#ifndef ULY_ALIGNED_MAX_CHUNKS
+#define ULY_ALIGNED_MAX_CHUNKS 4
 #endif
 
 // The fused kernel walks bands of one block each when set, else flat blocks
@@ -66,7 +67,7 @@ static uint64_t relayout_table(const ulysses::Plan &p, int mode, ulysses::Relayo
         // pieces of unequal width: bands aligned on rows, one chunk per block
         if (ULY_ALIGNED) {
             const uint64_t n = ulysses::fill_relayout_aligned(
-                p, mode, ulysses::relayout_vectors_per_block(), ULY_ALIGNED_MAX_ROWS, a);
+                p, mode, ulysses::relayout_vectors_per_block(), ULY_ALIGNED_MAX_CHUNKS, a);
             if (n != 0) return n;
         }
         return ulysses::fill_relayout_vbands(p, mode, ULY_VBAND, a);

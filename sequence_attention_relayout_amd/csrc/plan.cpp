@@ -253,7 +253,7 @@ uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
     return blocks;
 }
 
-uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_rows,
+uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_chunks,
                                RelayoutArgs *a) {
     const ModeGeom &g = p.mode[mode];
     // Row widths of the k-th piece of a group: the same for every group
@@ -276,7 +276,10 @@ uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uin
     while (y != 0) { const uint32_t t = gc % y; gc = y; y = t; }
     // R * vpr_k is a multiple of chunk_vecs for R = chunk_vecs / gc
     const uint32_t rows_per_band = chunk_vecs / gc;
-    if (max_rows != 0 && rows_per_band > max_rows) return 0;
+    if (max_chunks != 0) {
+        for (int k = 0; k < p.world; ++k)
+            if (uint64_t(rows_per_band) * vpr[k] > uint64_t(max_chunks) * chunk_vecs) return 0;
+    }
     clear_table(a);
     for (int r = 0; r < p.world; ++r) {
         a->src_plane[r] = static_cast<uint64_t>(g.src_plane[r] / 16);

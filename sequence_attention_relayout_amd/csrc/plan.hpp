@@ -94,9 +94,9 @@ uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, Relay
 // every piece's band a whole number of chunk_vecs-vector chunks, one chunk
 // per block, so blocks running side by side cover the same rows of every
 // piece.  Returns grid.x, or 0 without touching *a when the pieces of a group
-// all have the same width, or when max_rows != 0 and R exceeds it (then
-// fill_relayout_vbands applies).
-uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_rows,
+// all have the same width, or when max_chunks != 0 and some piece's band
+// would hold more than max_chunks chunks (then fill_relayout_vbands applies).
+uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_chunks,
                                RelayoutArgs *a);
 
 // Band height so that one band of the widest piece moves about

@@ -425,28 +425,30 @@ static void check_div32(std::mt19937_64 &rng) {
 }
 
 // When the row-aligned table applies: pieces of unequal width whose
-// whole-chunk bands need at most max_rows rows.
+// whole-chunk bands hold at most max_chunks chunks of 64 vectors per piece.
 static void check_aligned_choice() {
-    struct Case { std::vector<int64_t> H; uint32_t max_rows; uint32_t rows; };
+    struct Case { int64_t d; std::vector<int64_t> H; uint32_t max_chunks; uint32_t rows; };
     const Case cases[] = {
-        {{6, 6, 6, 6, 4, 4, 4, 4}, 2, 2},   // widths 96/64 vectors: bands of 2 rows
-        {{4, 4, 4, 4, 2, 2, 2, 2}, 2, 2},   // 64/32
-        {{8, 8, 4, 4}, 2, 1},               // 128/64: one row
-        {{6, 6, 6, 6, 5, 5, 5, 5}, 2, 0},   // 96/80 would need 4 rows: vector bands
-        {{6, 6, 6, 6, 5, 5, 5, 5}, 0, 4},   // ... unless uncapped
-        {{5, 5, 5, 5}, 2, 0},               // equal widths: vector bands
-        {{5, 0, 5, 5}, 2, 0},               // an empty piece does not count
+        {128, {6, 6, 6, 6, 4, 4, 4, 4}, 4, 2},   // widths 96/64 vectors: 2 rows, 3/2 chunks
+        {128, {4, 4, 4, 4, 2, 2, 2, 2}, 4, 2},   // 64/32: 2 rows, 2/1 chunks
+        {128, {8, 8, 4, 4}, 4, 1},               // 128/64: 1 row, 2/1 chunks
+        {128, {8, 8, 8, 6}, 4, 2},               // 128/96: 2 rows, 4/3 chunks
+        {128, {6, 6, 6, 6, 5, 5, 5, 5}, 4, 0},   // 96/80: 4 rows, 6/5 chunks: vector bands
+        {128, {6, 6, 6, 6, 5, 5, 5, 5}, 0, 4},   // ... unless uncapped
+        {256, {6, 6, 6, 6, 6, 5, 5}, 4, 0},      // 192/160: 2 rows but 6/5 chunks
+        {128, {5, 5, 5, 5}, 4, 0},               // equal widths: vector bands
+        {128, {5, 0, 5, 5}, 4, 0},               // an empty piece does not count
     };
     for (const Case &c : cases) {
         const int world = static_cast<int>(c.H.size());
         std::vector<int64_t> S(world, 7);
         Plan p;
         std::string msg;
-        REQUIRE(plan_build(&p, world, 1, 128, S.data(), c.H.data(), 0, 0, &msg) == kOk, "plan");
+        REQUIRE(plan_build(&p, world, 1, c.d, S.data(), c.H.data(), 0, 0, &msg) == kOk, "plan");
         for (int mode = 0; mode < 2; ++mode) {
             RelayoutArgs a;
             std::memset(&a, 0x5A, sizeof a);
-            const uint64_t gx = fill_relayout_aligned(p, mode, 64, c.max_rows, &a);
+            const uint64_t gx = fill_relayout_aligned(p, mode, 64, c.max_chunks, &a);
             if (c.rows == 0) {
                 REQUIRE(gx == 0, "aligned table where vector bands apply");
             } else {

@@ -173,8 +173,8 @@ def test_many_tiny_random_geometries():
         if sum(head) == 0:
             head[int(rng.integers(0, world))] += 4
         widths = {h * d * esz // 16 for h in head if h}
-        g = int(np.gcd.reduce(list(widths)))
-        aligned += len(widths) > 1 and 64 // int(np.gcd(64, g)) <= 2
+        rows = 64 // int(np.gcd(64, int(np.gcd.reduce(list(widths)))))
+        aligned += len(widths) > 1 and rows * max(widths) <= 4 * 64
         plan = U.ulysses_plan_create(world, b, d, seq, head, dt, 1 << 30)
         wl = W.Workload("tiny random", world, b, d, seq, head)
         for mode in (0, 1):
@@ -212,10 +212,11 @@ def test_many_tiny_random_geometries():
 @pytest.mark.parametrize("head", [[6, 6, 6, 6, 4, 4, 4, 4], [4, 4, 4, 4, 2, 2, 2, 2],
                                   [8, 8, 4, 4], [4, 2, 0, 2, 6]])
 def test_unequal_head_widths_row_aligned(head):
-    """Head splits whose rows differ in width and make bands of whole chunks
-    within two rows: the relayout walks row-aligned chunks (one band of every
-    piece covers the same rows).  Uneven sequence splits, two batch planes,
-    every element compared in both modes."""
+    """Head splits whose rows differ in width and whose bands of whole
+    64-vector chunks hold at most four chunks per piece: the relayout walks
+    row-aligned chunks (one band of every piece covers the same rows).
+    Uneven sequence splits, two batch planes, every element compared in both
+    modes."""
     world = len(head)
     seq = W.seeded_partition(11, 2001 * world, world)
     H.say(f"case: unequal head widths W={world} seq={seq} head={head}")
