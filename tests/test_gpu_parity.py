@@ -154,8 +154,9 @@ def test_many_tiny_random_geometries():
     """300 tiny random geometries in one process (W 1-8, splits 0-40 with
     zeros, head counts 0-12, b 1-3, every dtype and several row widths; a
     third of them with head counts in multiples of 4 so that unequal widths
-    take the row-aligned walk): both modes, the plane-at-a-time call, and
-    the fused call for bf16, every element against the oracle."""
+    take the row-aligned walk): both modes, two tensors in one launch, the
+    plane-at-a-time call, and the fused call for bf16, every element against
+    the oracle."""
     rng = np.random.default_rng(9000)
     aligned = 0
     for case in range(300):
@@ -185,6 +186,15 @@ def test_many_tiny_random_geometries():
             except AssertionError:
                 H.say(f"failing case {case}: {dt} W={world} b={b} d={d} seq={seq} head={head}")
                 raise
+            if mode == 0 and case % 2 == 0:   # two tensors in one launch (grid.z = 2)
+                xs2 = W.make_shards(wl, 0, dt, 9500 + case, DEV)
+                o1 = [torch.empty(s_, dtype=W.torch_dtype(dt), device=DEV)
+                      for s_ in dst_shapes(plan, 0)]
+                o2 = [torch.empty_like(t) for t in o1]
+                U.ulysses_a2a_4d_multi(plan, 0, [xs, xs2], [o1, o2])
+                torch.cuda.synchronize()
+                check_full(0, b, d, seq, head, xs, o1)
+                check_full(0, b, d, seq, head, xs2, o2)
             if mode == 1:
                 win = [torch.empty(max(1, U.ulysses_plan_window_bytes(plan, 1)), dtype=torch.uint8,
                                    device=DEV) for _ in range(world)]
