@@ -140,10 +140,13 @@ __global__ void __launch_bounds__(BLOCK) relayout_kernel(const RelayoutArgs a) {
         if (ok[k]) store16<NTS>(db + doff[k] * 16, v[k]);
 }
 
-// Row-band traversal: block x moves one band of rows of one piece; the W
-// pieces that share a row-sharded shard take consecutive blocks band by
-// band, so blocks running side by side sweep whole contiguous rows of that
-// shard and W contiguous streams of the head-sharded side.
+// Band traversals: the W pieces that share a row-sharded shard take
+// consecutive blocks band by band, so blocks running side by side sweep whole
+// contiguous rows of that shard and W contiguous streams of the head-sharded
+// side.  A band is band_vecs vectors of a piece (the default), band_rows rows
+// of a piece (walked in chunks of BLOCK * UNROLL vectors), or, when the
+// pieces differ in row width, band_rows rows of every piece cut into chunks
+// with one chunk per block (RelayoutArgs describes the three tables).
 template <int BLOCK, int UNROLL, bool NTL, bool NTS>
 __global__ void __launch_bounds__(BLOCK) relayout_band_kernel(const RelayoutArgs a) {
     const uint32_t x = blockIdx.x;
