@@ -51,6 +51,20 @@ MUTANTS = [
      "part[k] = part[k] + part[k + n / 2];"),
     ("tree drops the odd partial", "part[k] = part[2 * k] + part[2 * k + 1];",
      "part[k] = part[2 * k] + part[2 * k];"),
+    ("first cosine product contracted into the subtract",
+     "o[2 * p] = float_to_bf16_rne(a - bb);",
+     "o[2 * p] = float_to_bf16_rne(fmaf(y[2 * p], c, -bb));"),
+    ("first sine product contracted into the subtract",
+     "o[2 * p] = float_to_bf16_rne(a - bb);",
+     "o[2 * p] = float_to_bf16_rne(fmaf(-y[2 * p + 1], s, a));"),
+    ("second sine product contracted into the add",
+     "o[2 * p + 1] = float_to_bf16_rne(cc + dd);",
+     "o[2 * p + 1] = float_to_bf16_rne(fmaf(y[2 * p], s, dd));"),
+    ("second cosine product contracted into the add",
+     "o[2 * p + 1] = float_to_bf16_rne(cc + dd);",
+     "o[2 * p + 1] = float_to_bf16_rne(fmaf(y[2 * p + 1], c, cc));"),
+    ("gain folded into inv first", "        y[i] = (xf[i] * inv) * gamma[i];",
+     "        y[i] = xf[i] * (inv * gamma[i]);"),
 ]
 
 

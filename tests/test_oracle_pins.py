@@ -6,8 +6,11 @@ same permutation (numpy slicing and concatenation, the reshape/transpose of
 the permute + all_to_all_single + permute baseline), brute-force decoding of
 index-coded inputs, invariants (identity at one rank, mode 1 inverts mode 0,
 every element moved exactly once), closed forms of the rotary table, torch's
-own float -> bfloat16 conversion, and a float64 evaluation of RMSNorm and of
-RoPE written as a complex multiplication.
+own float -> bfloat16 conversion, a float64 evaluation of RMSNorm and of
+RoPE written as a complex multiplication, and rows worked by hand in exact
+rational arithmetic whose bf16 outputs depend on each rounding step the fused
+row fixes (summation order, rotation products rounded one by one, the gain
+applied after the norm).
 """
 import math
 
@@ -463,3 +466,164 @@ def test_fused_rejects_unsupported_d():
         oracle.qknorm_rope_mode0(1, 24, [1], [1], [np.zeros((1, 1, 1, 24), np.uint16)],
                                  np.ones(24, np.float32), 1e-6,
                                  np.ones((1, 12), np.float32), np.zeros((1, 12), np.float32))
+
+
+# ---------------------------------------------------------------------------
+# the fused row's remaining rounding steps, pinned by hand-worked rows
+# ---------------------------------------------------------------------------
+#
+# Exact rational arithmetic with IEEE binary32 rounding (nearest, ties to
+# even), written here from the format's definition, so that the expected bits
+# below are derived independently of the oracle's C code.
+
+from fractions import Fraction as Q
+
+
+def f32_round(q):
+    """The binary32 value nearest to the rational q (ties to even; normal
+    range only, which every value below stays in)."""
+    if q == 0:
+        return Q(0)
+    sign = -1 if q < 0 else 1
+    a = abs(q)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    scaled = a * 2 ** 23                     # in [2^23, 2^24)
+    lo = scaled.numerator // scaled.denominator
+    rem = scaled - lo
+    if rem > Q(1, 2) or (rem == Q(1, 2) and lo % 2 == 1):
+        lo += 1
+    return sign * Q(lo) * Q(2) ** (e - 23)
+
+
+def f32_sqrt(q):
+    """Correctly rounded binary32 square root of a positive rational: the
+    candidate r whose rounding interval [r - ulp/2, r + ulp/2] holds sqrt(q)."""
+    r = f32_round(Q(math.sqrt(float(q))))
+    for _ in range(4):
+        ulp = Q(2) ** (math.frexp(float(r))[1] - 24)
+        lo, hi = r - ulp / 2, r + ulp / 2
+        if lo * lo <= q <= hi * hi:
+            return r
+        r = r + ulp if hi * hi < q else r - ulp
+    raise AssertionError("no correctly rounded candidate")
+
+
+def f32_bits(q):
+    return int(np.float32(float(q)).view(np.uint32))
+
+
+def bf16_bits(q):
+    """bf16 (nearest, ties to even) of a binary32 value given exactly."""
+    u = f32_bits(q)
+    lsb = (u >> 16) & 1
+    return ((u + 0x7FFF + lsb) >> 16) & 0xFFFF
+
+
+def fused_one_row(d, x, gamma, cos_row, sin_row, eps):
+    """The oracle's fused output of one row (W = 1, b = 1, one head, position
+    0, tables of one row given explicitly)."""
+    row = np.zeros(d, np.float64)
+    row[:len(x)] = x
+    g = np.ones(d, np.float32)
+    g[:len(gamma)] = gamma
+    c = np.ones((1, d // 2), np.float32)
+    s = np.zeros((1, d // 2), np.float32)
+    c[0, :len(cos_row)] = cos_row
+    s[0, :len(sin_row)] = sin_row
+    xs = [torch_bf16_bits(row).reshape(1, 1, 1, d)]
+    return oracle.qknorm_rope_mode0(1, d, [1], [1], xs, g, eps, c, s)[0].reshape(d)
+
+
+E11, E12 = Q(1, 2 ** 11), Q(1, 2 ** 12)
+# Rows whose rotation outputs depend on each product being rounded on its
+# own: y = (x * inv) * gamma with x = 1/2 and inv = 2 exactly, so y = gamma.
+ROTATION_Y = [1 + E12, 1, 1, 1 + E12, 1 + E12, 1, 1, 1 + E12]
+ROTATION_COS = [1 + E12, 1 + E11, -(1 + E11), -(1 + E12)]
+ROTATION_SIN = [1 + E11, 1 + E12, 1 + E12, 1 + E11]
+
+
+def rotation_row(d):
+    """Elements 0..7 are 1/2 (sum of squares 2); for d = 128, elements 8..11
+    hold 4, 3, 2, 1 (a second partial of 30), so the mean square is 1/4 at
+    both d and inv = 1/sqrt(1/4 + 0) = 2 exactly."""
+    x = [0.5] * 8 + ([4.0, 3.0, 2.0, 1.0] if d == 128 else [])
+    return x, [float(v) for v in ROTATION_Y]
+
+
+@pytest.mark.parametrize("d", [8, 128])
+def test_rotation_products_rounded_separately(d):
+    """Each rotation product is rounded before the add or subtract (no fused
+    multiply-add), worked by hand for four pairs at position 0 with an
+    explicit table row:
+      pair 0: y = (1 + 2^-12, 1), cos 1 + 2^-12, sin 1 + 2^-11.
+        y0*cos = 1 + 2^-11 + 2^-24, a tie that goes to the even 1 + 2^-11, and
+        y1*sin = 1 + 2^-11, so o0 = +0; contracting y0*cos into the subtract
+        would leave 2^-24 (bf16 0x3380).  o1 = (1 + 2^-11 + 2^-12 + 2^-23) +
+        (1 + 2^-12) = 2 + 2^-10 + 2^-23, a tie to 2 + 2^-10, bf16 2.0.
+      pair 1: y = (1, 1 + 2^-12), cos 1 + 2^-11, sin 1 + 2^-12: the second
+        product of o2 is the rounded one, o2 = +0 (a contraction of it:
+        -2^-24), o3 = 2.0.
+      pair 2: y = (1 + 2^-12, 1), cos -(1 + 2^-11), sin 1 + 2^-12: o4 =
+        -(2 + 2^-10 + 2^-23) -> -2.0; o5 = (1 + 2^-11) - (1 + 2^-11) = +0 (a
+        contraction of y4*sin: 2^-24).
+      pair 3: y = (1, 1 + 2^-12), cos -(1 + 2^-12), sin 1 + 2^-11: o6 = -2.0,
+        o7 = +0 (a contraction of y7*cos: -2^-24).
+    At d = 128 elements 8..11 (4, 3, 2, 1, gain 1, identity rotation) come
+    out as 2x."""
+    x, gamma = rotation_row(d)
+    out = fused_one_row(d, x, gamma, [float(v) for v in ROTATION_COS],
+                        [float(v) for v in ROTATION_SIN], 0.0)
+    # the hand derivation, step by step in exact arithmetic
+    y = ROTATION_Y
+    want = []
+    for p in range(4):
+        c, s = ROTATION_COS[p], ROTATION_SIN[p]
+        a, b = f32_round(y[2 * p] * c), f32_round(y[2 * p + 1] * s)
+        e, f = f32_round(y[2 * p] * s), f32_round(y[2 * p + 1] * c)
+        want += [bf16_bits(f32_round(a - b)), bf16_bits(f32_round(e + f))]
+    assert want == [0x0000, 0x4000, 0x0000, 0x4000, 0xC000, 0x0000, 0xC000, 0x0000]
+    # each contraction would change one output
+    contracted = [bf16_bits(f32_round(y[0] * ROTATION_COS[0] - f32_round(y[1] * ROTATION_SIN[0]))),
+                  bf16_bits(f32_round(f32_round(y[2] * ROTATION_COS[1]) - y[3] * ROTATION_SIN[1])),
+                  bf16_bits(f32_round(y[4] * ROTATION_SIN[2] + f32_round(y[5] * ROTATION_COS[2]))),
+                  bf16_bits(f32_round(f32_round(y[6] * ROTATION_SIN[3]) + y[7] * ROTATION_COS[3]))]
+    assert contracted == [0x3380, 0xB380, 0x3380, 0xB380]
+    if d == 128:
+        want += [0x4100, 0x40C0, 0x4080, 0x4000]      # 8, 6, 4, 2
+    want += [0] * (d - len(want))
+    assert [int(v) for v in out] == want
+
+
+# (x * inv) * gamma against x * (inv * gamma): one non-zero element x0 = 1.5,
+# eps = 0, identity rotation.  The gains were found by a search over random
+# binary32 values in [0.5, 1.5) for a row whose bf16 output depends on the
+# order of the two products.
+GAIN_ORDER = {8: (0x3F9EBED7, 0x3FF15BF0, 0x4061, 0x4060),
+              128: (0x3F9D54CD, 0x40F15BF0, 0x415E, 0x415F)}
+
+
+@pytest.mark.parametrize("d", [8, 128])
+def test_gain_applied_after_the_norm(d):
+    """y = (x * inv) * gamma, two products rounded in that order.  With one
+    non-zero element x0 = 1.5 and eps = 0: ss = 2.25, ms = 2.25 / d, inv =
+    1 / sqrt(ms) with both steps correctly rounded (0x3FF15BF0 at d = 8,
+    0x40F15BF0 at d = 128, four times it).  For the gain listed, the bf16
+    output of element 0 is 0x4061 (d = 8) or 0x415E (d = 128) in this order,
+    and 0x4060 or 0x415F with the gain folded into inv first."""
+    g_bits, inv_bits, want0, other0 = GAIN_ORDER[d]
+    g0 = Q(float(np.uint32(g_bits).view(np.float32)))
+    x0 = Q(3, 2)
+    ms = f32_round(x0 * x0 / d)
+    inv = f32_round(1 / f32_sqrt(ms))
+    assert f32_bits(inv) == inv_bits
+    assert bf16_bits(f32_round(f32_round(x0 * inv) * g0)) == want0
+    assert bf16_bits(f32_round(x0 * f32_round(inv * g0))) == other0
+    out = fused_one_row(d, [1.5], [float(g0)], [], [], 0.0)
+    assert int(out[0]) == want0
+    assert np.all(out[1:] == 0)
