@@ -19,12 +19,17 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              comes from the rocprofv3 counter
              summary in profiles/ when it was taken on the current kernel
              source, else null;
-  cpu_baseline  the CPU oracle (single thread) on a bounded sample;
+  value_mall_cold  the same step with the 256 MB Infinity Cache written
+             over between launches (per-mode medians), beside `value`;
+  cpu_baseline  the CPU oracle on the step's geometry: its loops on all
+             the host cores the process may use (value), and single-threaded;
   rows       the other hot-path rows timed after the step: uneven W=7 in
-             four dtypes, the plane-at-a-time QKV pack, the fused QK-norm +
-             RoPE scatter; plus a same-run device-to-device copy (torch) and
-             this GPU's read / write / copy ceilings for the relayout's access
-             shape (probe/hbm_probe, run as a child process first).
+             four dtypes, unequal head widths, q/k/v in one launch, the
+             plane-at-a-time QKV pack through windows and straight into the
+             destination, the fused QK-norm + RoPE scatter; plus a same-run
+             device-to-device copy (torch) and this GPU's read / write / copy
+             ceilings for 16-byte vectors (hbm_probe, run as a child process
+             first).
 """
 import argparse
 import hashlib
@@ -42,6 +47,23 @@ COUNTERS = os.path.join(ROOT, "profiles", "relayout_w8_wan720p_counters.json")
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+PROBE_SRC = os.path.join(ROOT, "hbm_probe.hip")
+PROBE = os.path.join(ROOT, "hbm_probe")
+
+
+def build_probe(verbose=False):
+    """Compiles hbm_probe.hip (this GPU's HBM read / write / copy ceilings),
+    a standalone gfx950 program that only this benchmark runs."""
+    import subprocess
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = [os.path.join(rocm, "bin", "hipcc"), "-O3", "-std=c++17", "--offload-arch=gfx950",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PROBE_SRC, "-o", PROBE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return PROBE
 
 
 def kernel_source_hash():
@@ -88,10 +110,11 @@ def timed(fn, reps, stream, torch, warmup=3):
     return statistics.median(ts), min(ts)
 
 
-def cpu_baseline(reps=5, budget_s=30.0):
-    """The oracle as it is (plain index loops, one thread) on the whole
-    workload's geometry: one mode 0 and one mode 1 per repetition, median
-    rate; stops early once `budget_s` seconds are spent."""
+def cpu_baseline(reps=3):
+    """The oracle as it is on the whole step's geometry (one mode 0 and one
+    mode 1 per run, median of `reps` runs): its loops on every host core this
+    process may use (the threaded entry point hands destination rows to
+    threads), and single-threaded."""
     import numpy as np
     import oracle
     world, per_rank, heads, d = 8, 9450, 5, 128
@@ -102,14 +125,19 @@ def cpu_baseline(reps=5, budget_s=30.0):
     ys_in = [rng.integers(0, 1 << 16, (1, per_rank * world, heads, d), dtype=np.uint16)
              for _ in range(world)]
     nbytes = 2 * 2 * (per_rank * world) * (heads * world) * d * 2
-    times = []
-    t_start = time.perf_counter()
-    while len(times) < reps and (not times or time.perf_counter() - t_start < budget_s):
-        t0 = time.perf_counter()
-        oracle.a2a_4d(0, 1, d, seq, head, xs)
-        oracle.a2a_4d(1, 1, d, seq, head, ys_in)
-        times.append(time.perf_counter() - t0)
-    dt = statistics.median(times)
+    cores = len(os.sched_getaffinity(0))
+
+    def rate(threads):
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.a2a_4d(0, 1, d, seq, head, xs, threads=threads)
+            oracle.a2a_4d(1, 1, d, seq, head, ys_in, threads=threads)
+            times.append(time.perf_counter() - t0)
+        return nbytes / statistics.median(times) / 1e9, statistics.median(times), sum(times)
+
+    all_gbs, all_dt, all_s = rate(cores)
+    one_gbs, one_dt, one_s = rate(1)
     cpu = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -119,12 +147,13 @@ def cpu_baseline(reps=5, budget_s=30.0):
                     break
     except OSError:
         pass
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "cpu": cpu, "host_cores_available": len(os.sched_getaffinity(0)),
-            "sample": f"the full step's geometry (W=8, 75,600 tokens, n=40, d=128, bf16): one "
-                      f"mode 0 and one mode 1 on the oracle's plain index loops, single thread, "
-                      f"median of {len(times)} runs of {dt:.1f} s each",
-            "seconds": round(sum(times), 2)}
+    sample = ("the full step's geometry (W=8, 75,600 tokens, n=40, d=128, bf16): one mode 0 and "
+              f"one mode 1 on the oracle's plain index loops, median of {reps} runs")
+    return {"value": round(all_gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu": cpu, "sample": sample + f" ({all_dt:.2f} s each, {cores} threads)",
+            "single_thread": {"value": round(one_gbs, 3), "unit": "GB/s", "cores": 1,
+                              "seconds_per_run": round(one_dt, 2)},
+            "seconds": round(all_s + one_s, 2)}
 
 
 def hbm_ceilings():
@@ -132,7 +161,7 @@ def hbm_ceilings():
     process; returns the best of its launch shapes for each kind,
     {"copy": GB/s, "read": GB/s, "write": GB/s}, or None."""
     import subprocess
-    exe = os.path.join(ROOT, "sequence_attention_relayout_amd", "probe", "hbm_probe")
+    exe = PROBE
     if not os.path.exists(exe):
         log("hbm probe not built; skipping the ceilings")
         return None
@@ -297,7 +326,9 @@ def main():
                    "world": 8, "b": 1, "s_global": 75600, "n_global": 40, "d": 128,
                    "bytes_per_step": step_bytes, "parallelism": "none (one GPU)"},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "relayout_band_kernel", "achieved": round(achieved, 1),
+        "value_mall_cold": round(step_bytes / ((statistics.median(c0) + statistics.median(c1))
+                                               * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "relayout_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_GBS, 4),
                      "traffic": traffic_from_profile(),
                      "bytes_per_launch": bytes0, "avg_launch_us": round(launch_ms * 1e3, 2),
@@ -392,34 +423,11 @@ def time_rows(U, W, torch, dev, stream, reps=20):
         tiny_step()
     torch.cuda.synchronize()
     host_us = (time.perf_counter() - t0) / 1000 * 1e6
-    # the same two launches captured once in a HIP graph and replayed: the
-    # device-side floor without the per-call host path
-    def tiny_step_current_stream():
-        U.ulysses_a2a_4d(plan, 0, xs, ys)
-        U.ulysses_a2a_4d(plan, 1, ys, zs)
-
-    side = torch.cuda.Stream()
-    side.wait_stream(stream)
-    with torch.cuda.stream(side):
-        tiny_step_current_stream()          # warm-up on the capture stream
-    stream.wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        tiny_step_current_stream()
-    for z in zs:
-        z.zero_()
-    med_graph, _ = timed(graph.replay, 50, stream, torch)
-    torch.cuda.synchronize()
-    roundtrip = all(torch.equal(x.view(torch.int16), z.view(torch.int16)) for x, z in zip(xs, zs))
     rows["w2_tiny_latency"] = {"step_median_us": round(med_tiny * 1e3, 2),
                                "host_us_per_call": round(host_us, 2),
-                               "graph_replay_step_median_us": round(med_graph * 1e3, 2),
-                               "graph_replay_roundtrip_exact": roundtrip,
                                "note": "mode 0 + mode 1 of the two-rank example (65,536 B "
-                                       "per mode); host time per ABI call through Python; the "
-                                       "same two launches replayed from one captured HIP graph"}
-    del graph, xs, ys, zs
+                                       "per mode); host time per ABI call through Python"}
+    del xs, ys, zs
 
     # q, k and v of the timed geometry: one launch against three
     wl = wls["w8_wan720p"]
@@ -458,6 +466,8 @@ def time_rows(U, W, torch, dev, stream, reps=20):
     torch.cuda.empty_cache()
     log("multi-tensor rows done")
 
+    # the FastVideo pack, plane at a time: through the windows (relayout,
+    # then copy-out), straight into the destination planes, and in one pass
     wl = wls["w4_qkv_chunked"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16",
                                  wl.window_cap_bytes)
@@ -466,16 +476,25 @@ def time_rows(U, W, torch, dev, stream, reps=20):
           for r in range(wl.world)]
     win = [torch.empty(U.ulysses_plan_window_bytes(plan, 0), dtype=torch.uint8, device=dev)
            for _ in range(wl.world)]
-    med, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win, h), 3, stream, torch)
     relayout_bytes = U.ulysses_plan_bytes(plan, 0)
+    staged, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win, h), 5, stream,
+                      torch)
+    direct, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, None, h), 5, stream,
+                      torch)
+    one_pass, _ = timed(lambda: U.ulysses_a2a_4d(plan, 0, xs, ys, h), 5, stream, torch)
     rows["w4_qkv_chunked_mode0"] = {
-        "gbs_relayout_bytes": round(relayout_bytes / (med * 1e-3) / 1e9, 1),
-        "gbs_moved_bytes": round(2 * relayout_bytes / (med * 1e-3) / 1e9, 1),
-        "median_us": round(med * 1e3, 1), "relayout_bytes": relayout_bytes,
-        "moved_bytes_incl_window_copy": 2 * relayout_bytes}
-    med, _ = timed(lambda: U.ulysses_a2a_4d(plan, 0, xs, ys, h), 3, stream, torch)
-    rows["w4_qkv_direct_mode0"] = {"gbs": round(relayout_bytes / (med * 1e-3) / 1e9, 1),
-                                   "median_us": round(med * 1e3, 1)}
+        "staged_gbs_relayout_bytes": round(relayout_bytes / (staged * 1e-3) / 1e9, 1),
+        "staged_gbs_moved_bytes": round(2 * relayout_bytes / (staged * 1e-3) / 1e9, 1),
+        "staged_median_us": round(staged * 1e3, 1),
+        "direct_gbs": round(relayout_bytes / (direct * 1e-3) / 1e9, 1),
+        "direct_median_us": round(direct * 1e3, 1),
+        "staged_over_direct": round(staged / direct, 3),
+        "one_pass_gbs": round(relayout_bytes / (one_pass * 1e-3) / 1e9, 1),
+        "one_pass_median_us": round(one_pass * 1e3, 1),
+        "relayout_bytes": relayout_bytes,
+        "note": "staged: per plane, relayout into the W windows then copy-out (twice the "
+                "bytes); direct: per plane, relayout straight into the destination plane (the "
+                "window is the output slice); one pass: all three planes in one launch"}
     del xs, ys, win
     torch.cuda.empty_cache()
     log("chunked rows done")

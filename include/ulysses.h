@@ -172,10 +172,16 @@ int ulysses_a2a_4d_multi(const ulysses_plan *plan, int mode, int ntensors,
  *
  *   window  host array of W device pointers, each to at least
  *           ulysses_plan_window_bytes(plan, mode) bytes, 16-byte aligned,
- *           overlapping no source, destination or other window.
+ *           overlapping no source, destination or other window;
+ *           or NULL: the window of plane p is plane p of the destination
+ *           itself, so each plane's relayout writes straight into its final
+ *           place and there is no copy-out (fast-ulysses 0.2.1 "Key
+ *           features", "Performance" and "API": an output allocated up
+ *           front and passed as out= removes the copy-out).
  *
  * EINVAL when the plan has no cap (window_cap_bytes == 0); EWINDOW when
- * ulysses_plan_window_bytes(plan, mode) exceeds the cap.
+ * ulysses_plan_window_bytes(plan, mode) exceeds the cap (with or without
+ * windows: the destination plane then takes the window's place).
  */
 int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const *src,
                            void *const *dst, void *const *window, hipStream_t stream);

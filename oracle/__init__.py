@@ -43,6 +43,9 @@ def _load():
     lib.oracle_a2a_4d.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _p, _p,
                                   _p, _p]
     lib.oracle_a2a_4d.restype = ctypes.c_int
+    lib.oracle_a2a_4d_threads.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _p, _p,
+                                          _p, _p, ctypes.c_int]
+    lib.oracle_a2a_4d_threads.restype = ctypes.c_int
     lib.oracle_a2a_4d_sample.argtypes = [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
                                          _p, _p, _p, _i64, _p, _p]
     lib.oracle_a2a_4d_sample.restype = ctypes.c_int
@@ -55,6 +58,9 @@ def _load():
     lib.oracle_qknorm_rope_mode0.argtypes = [ctypes.c_int, _i64, _i64, _p, _p, _p, _p,
                                              _p, ctypes.c_float, _p, _p]
     lib.oracle_qknorm_rope_mode0.restype = ctypes.c_int
+    lib.oracle_qknorm_rope_mode0_threads.argtypes = [ctypes.c_int, _i64, _i64, _p, _p, _p, _p,
+                                                     _p, ctypes.c_float, _p, _p, ctypes.c_int]
+    lib.oracle_qknorm_rope_mode0_threads.restype = ctypes.c_int
     lib.oracle_qknorm_rope_mode0_sample.argtypes = [ctypes.c_int, _i64, _i64, _p, _p,
                                                     _p, _p, ctypes.c_float, _p, _p,
                                                     _i64, _p, _p]
@@ -103,8 +109,10 @@ def window_bytes(mode, d, esz, seq_splits, head_splits):
     return int(v)
 
 
-def a2a_4d(mode, b, d, seq_splits, head_splits, srcs):
-    """Full relayout of the W source shards; returns the W destination shards."""
+def a2a_4d(mode, b, d, seq_splits, head_splits, srcs, threads=1):
+    """Full relayout of the W source shards; returns the W destination shards.
+    threads > 1 hands whole destination rows to that many threads (the same
+    loops; identical results)."""
     s, h = _splits(seq_splits, head_splits)
     world = len(s)
     if len(srcs) != world:
@@ -115,8 +123,13 @@ def a2a_4d(mode, b, d, seq_splits, head_splits, srcs):
         if tuple(a.shape) != want or a.dtype != dtype:
             raise ValueError(f"source {r}: shape {a.shape} {a.dtype}, want {want} {dtype}")
     dsts = [np.empty(shape(mode, b, d, s, h, r, True), dtype=dtype) for r in range(world)]
-    _check(_load().oracle_a2a_4d(mode, world, b, d, dtype.itemsize, s.ctypes.data,
-                                 h.ctypes.data, _ptrs(srcs), _ptrs(dsts)), "a2a_4d")
+    if threads > 1:
+        _check(_load().oracle_a2a_4d_threads(mode, world, b, d, dtype.itemsize, s.ctypes.data,
+                                             h.ctypes.data, _ptrs(srcs), _ptrs(dsts),
+                                             int(threads)), "a2a_4d")
+    else:
+        _check(_load().oracle_a2a_4d(mode, world, b, d, dtype.itemsize, s.ctypes.data,
+                                     h.ctypes.data, _ptrs(srcs), _ptrs(dsts)), "a2a_4d")
     return dsts
 
 
@@ -157,8 +170,10 @@ def rope_table(theta, s_global, d):
     return c, sn
 
 
-def qknorm_rope_mode0(b, d, seq_splits, head_splits, srcs, gamma, eps, cos_tab, sin_tab):
-    """Fused mode 0 of one bf16 tensor (uint16 arrays); returns W shards."""
+def qknorm_rope_mode0(b, d, seq_splits, head_splits, srcs, gamma, eps, cos_tab, sin_tab,
+                      threads=1):
+    """Fused mode 0 of one bf16 tensor (uint16 arrays); returns W shards.
+    threads > 1 hands whole destination rows to that many threads."""
     s, h = _splits(seq_splits, head_splits)
     world = len(s)
     for r, a in enumerate(srcs):
@@ -171,10 +186,13 @@ def qknorm_rope_mode0(b, d, seq_splits, head_splits, srcs, gamma, eps, cos_tab, 
             or sin_tab.shape != cos_tab.shape:
         raise ValueError("gamma must be [d], tables [s_global, d/2]")
     dsts = [np.empty(shape(0, b, d, s, h, r, True), dtype=np.uint16) for r in range(world)]
-    _check(_load().oracle_qknorm_rope_mode0(world, b, d, s.ctypes.data, h.ctypes.data,
-                                            _ptrs(srcs), _ptrs(dsts), gamma.ctypes.data,
-                                            float(eps), cos_tab.ctypes.data,
-                                            sin_tab.ctypes.data), "qknorm_rope_mode0")
+    args = (world, b, d, s.ctypes.data, h.ctypes.data, _ptrs(srcs), _ptrs(dsts),
+            gamma.ctypes.data, float(eps), cos_tab.ctypes.data, sin_tab.ctypes.data)
+    if threads > 1:
+        _check(_load().oracle_qknorm_rope_mode0_threads(*args, int(threads)),
+               "qknorm_rope_mode0")
+    else:
+        _check(_load().oracle_qknorm_rope_mode0(*args), "qknorm_rope_mode0")
     return dsts
 
 

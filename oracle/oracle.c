@@ -30,6 +30,12 @@
  * -ffp-contract=off and no fast-math: every float operation below is one
  * IEEE single-precision operation in the written order.
  *
+ * The *_threads entry points run the very same loops with an OpenMP pragma
+ * that hands whole destination rows to `threads` threads: each row is
+ * computed by one thread exactly as in the single-threaded form, so the
+ * results are identical; the threads only shorten the wall time (the
+ * benchmark's all-cores baseline and the full-size checks use them).
+ *
  * Return codes: 0 on success, -1 on invalid arguments (nothing written).
  */
 #include <math.h>
@@ -175,31 +181,50 @@ static const unsigned char *source_of(const geom_t *g, int mode,
 
 /* Full relayout.  src[j] and dst[r] are host buffers laid out contiguously,
  * row-major, d innermost, with the shapes oracle_shape() reports. */
-int oracle_a2a_4d(int mode, int world, int64_t b, int64_t d, int64_t esz,
+static int a2a_4d(int mode, int world, int64_t b, int64_t d, int64_t esz,
                   const int64_t *seq_splits, const int64_t *head_splits,
-                  const void *const *src, void *const *dst)
+                  const void *const *src, void *const *dst, int threads)
 {
     geom_t g;
     int r;
-    int64_t bi, s, h, e, rows, heads;
     if (mode != 0 && mode != 1)
         return -1;
     if (geom_init(&g, world, b, d, esz, seq_splits, head_splits) != 0)
         return -1;
     for (r = 0; r < world; ++r) {
         unsigned char *out = (unsigned char *)dst[r];
-        rows = (mode == 0) ? g.s_global : g.S[r];
-        heads = (mode == 0) ? g.H[r] : g.n_global;
+        const int64_t rows = (mode == 0) ? g.s_global : g.S[r];
+        const int64_t heads = (mode == 0) ? g.H[r] : g.n_global;
+        int64_t bi, s;
+#pragma omp parallel for collapse(2) schedule(static) if (threads > 1) num_threads(threads)
         for (bi = 0; bi < b; ++bi)
-            for (s = 0; s < rows; ++s)
+            for (s = 0; s < rows; ++s) {
+                int64_t h, e;
                 for (h = 0; h < heads; ++h)
                     for (e = 0; e < d; ++e) {
                         int64_t at = (((bi * rows + s) * heads + h) * d + e) * esz;
                         memcpy(out + at, source_of(&g, mode, src, r, bi, s, h, e),
                                (size_t)esz);
                     }
+            }
     }
     return 0;
+}
+
+int oracle_a2a_4d(int mode, int world, int64_t b, int64_t d, int64_t esz,
+                  const int64_t *seq_splits, const int64_t *head_splits,
+                  const void *const *src, void *const *dst)
+{
+    return a2a_4d(mode, world, b, d, esz, seq_splits, head_splits, src, dst, 1);
+}
+
+int oracle_a2a_4d_threads(int mode, int world, int64_t b, int64_t d, int64_t esz,
+                          const int64_t *seq_splits, const int64_t *head_splits,
+                          const void *const *src, void *const *dst, int threads)
+{
+    if (threads < 1)
+        return -1;
+    return a2a_4d(mode, world, b, d, esz, seq_splits, head_splits, src, dst, threads);
 }
 
 /* The same definition evaluated at n chosen destination coordinates.
@@ -379,23 +404,25 @@ int oracle_row_sum_of_squares(int64_t d, const uint16_t *x, float *ss)
 /* Mode-0 relayout of one bf16 tensor (q or k) with RMSNorm over d and RoPE
  * at the GLOBAL sequence position of each destination row.  Tables are
  * [s_global][d/2] floats (oracle_rope_table), gamma has d floats. */
-int oracle_qknorm_rope_mode0(int world, int64_t b, int64_t d,
+static int qknorm_rope_mode0(int world, int64_t b, int64_t d,
                              const int64_t *seq_splits, const int64_t *head_splits,
                              const uint16_t *const *src, uint16_t *const *dst,
                              const float *gamma, float eps,
-                             const float *cos_tab, const float *sin_tab)
+                             const float *cos_tab, const float *sin_tab, int threads)
 {
     geom_t g;
-    int r, j;
-    int64_t bi, S, h;
+    int r;
     if (!fused_d_ok(d))
         return -1;
     if (geom_init(&g, world, b, d, 2, seq_splits, head_splits) != 0)
         return -1;
-    for (r = 0; r < world; ++r)
+    for (r = 0; r < world; ++r) {
+        int64_t bi, S;
+#pragma omp parallel for collapse(2) schedule(static) if (threads > 1) num_threads(threads)
         for (bi = 0; bi < b; ++bi)
             for (S = 0; S < g.s_global; ++S) {
-                j = seq_owner(&g, S);
+                int j = seq_owner(&g, S);
+                int64_t h;
                 for (h = 0; h < g.H[r]; ++h) {
                     const uint16_t *x = src[j]
                         + ((bi * g.S[j] + (S - g.seq_off[j])) * g.n_global
@@ -405,7 +432,30 @@ int oracle_qknorm_rope_mode0(int world, int64_t b, int64_t d,
                                   cos_tab + S * (d / 2), sin_tab + S * (d / 2));
                 }
             }
+    }
     return 0;
+}
+
+int oracle_qknorm_rope_mode0(int world, int64_t b, int64_t d,
+                             const int64_t *seq_splits, const int64_t *head_splits,
+                             const uint16_t *const *src, uint16_t *const *dst,
+                             const float *gamma, float eps,
+                             const float *cos_tab, const float *sin_tab)
+{
+    return qknorm_rope_mode0(world, b, d, seq_splits, head_splits, src, dst, gamma, eps,
+                             cos_tab, sin_tab, 1);
+}
+
+int oracle_qknorm_rope_mode0_threads(int world, int64_t b, int64_t d,
+                                     const int64_t *seq_splits, const int64_t *head_splits,
+                                     const uint16_t *const *src, uint16_t *const *dst,
+                                     const float *gamma, float eps,
+                                     const float *cos_tab, const float *sin_tab, int threads)
+{
+    if (threads < 1)
+        return -1;
+    return qknorm_rope_mode0(world, b, d, seq_splits, head_splits, src, dst, gamma, eps,
+                             cos_tab, sin_tab, threads);
 }
 
 /* The fused definition evaluated on n chosen destination rows.  rows is

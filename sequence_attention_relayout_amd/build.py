@@ -32,9 +32,9 @@ def _run(cmd, verbose):
 
 
 def build(verbose=False, defines=(), out=LIB, build_dir=BUILD, kernel_src=None):
-    """Compile and link; `defines` (e.g. ["ULY_UNROLL=8"]) override the
-    kernels' compile-time launch constants; `kernel_src` replaces
-    csrc/kernels.hip (for experiments built outside the package)."""
+    """Compile and link; `defines` are extra preprocessor definitions and
+    `kernel_src` replaces csrc/kernels.hip (for experiments built outside the
+    package)."""
     os.makedirs(build_dir, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     dflags = [f"-D{d}" for d in defines]
@@ -51,19 +51,6 @@ def build(verbose=False, defines=(), out=LIB, build_dir=BUILD, kernel_src=None):
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
-
-
-PROBE = os.path.join(PKG, "probe", "hbm_probe")
-
-
-def build_probe(verbose=False):
-    """The benchmark's HBM-ceiling probe (probe/hbm_probe.hip), a standalone
-    gfx950 executable; not part of the library."""
-    hipcc = os.path.join(ROCM, "bin", "hipcc")
-    _run([hipcc, "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
-          "-Xclang", "-packed-fp32-ops", os.path.join(PKG, "probe", "hbm_probe.hip"), "-o",
-          PROBE], verbose)
-    return PROBE
 
 
 C_CHECK = os.path.join(ROOT, "tests", "native", "abi_c_check")

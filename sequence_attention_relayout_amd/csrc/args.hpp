@@ -3,37 +3,25 @@
 // Plain C++ types only (no HIP headers), so the plan that fills them builds
 // and is unit-tested without a GPU.  Every block is passed to its kernel by
 // value through the kernarg segment; each stays under 4 KiB (checked below).
+// Offsets, pitches and sizes are in 16-byte vectors.
 #pragma once
 #include <cstdint>
 
 namespace ulysses {
 
 constexpr int kMaxWorld = 8;
-constexpr int kMaxPieces = kMaxWorld * kMaxWorld;
 // Tensors one relayout launch can move (q, k, v and a gate: QKVG).
 constexpr int kMaxTensors = 4;
 // A row of any shard is at most this many 16-byte vectors (512 KiB).  The
-// kernels split a block's vector range into rows with a 32-bit
-// multiply-high whose numerators stay below 2^16 under this bound.
+// kernels split a block's vectors into rows with a 32-bit multiply-high whose
+// numerators stay below 2^16 under this bound.
 constexpr uint32_t kMaxRowVectors = 32768;
-
-// One (source rank j -> destination rank r) region of one batch plane: `rows`
-// rows of `vpr` 16-byte vectors, contiguous within each row on both sides.
-// Offsets and pitches are in 16-byte vectors.
-struct PieceArgs {
-    uint32_t nvec;        // rows * vpr
-    uint32_t vpr;         // vectors per row
-    uint32_t magic;       // floor(2^32 / vpr) + 1 when vpr >= 2, unused when vpr == 1
-    uint32_t src_pitch;   // row pitch in the source shard
-    uint32_t dst_pitch;   // row pitch in the destination shard
-    uint32_t src_off;     // first vector within the source plane
-    uint32_t dst_off;     // first vector within the destination plane
-    uint32_t src_row0;    // sequence position of the piece's first source row
-                          // (global position of row 0; used by the fused path)
-    uint8_t j, r;         // source and destination rank
-    uint8_t vpr_s1, vpr_s2;   // shifts of the exact division by vpr (div32)
-    uint32_t vpr_m;           // multiplier of the exact division by vpr (div32)
-};
+// Threshold entries past the world; no key reaches them.
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+// Threads per block: one wave per block for the relayout and the plane copy,
+// four for the fused scatter.
+constexpr uint32_t kRelayoutBlock = 64;
+constexpr uint32_t kFusedBlock = 256;
 
 // floor(n / d) for every 32-bit n, from the multiplier and shifts that
 // div32_magic gives for d (Granlund & Montgomery, "Division by invariant
@@ -61,74 +49,91 @@ constexpr Div32Magic div32_magic(uint32_t d) {
                       static_cast<uint8_t>(l > 0 ? l - 1 : 0)};
 }
 
-// Launch table for one relayout pass: grid.x walks the pieces' blocks, grid.y
-// the batch planes, grid.z the tensors (all of one plan's geometry).  Block x
-// belongs to the piece p with blk_begin[p] <= x < blk_begin[p + 1]; unused
-// entries hold 0xFFFFFFFF.
+// Row split of the vectors of one shard: vector v of a plane sits at row
+// v / vpr, column v % vpr.  The block's first vector is split with div32
+// (any 32-bit numerator); a lane's offset from there (below 2^16) with one
+// multiply-high by magic = floor(2^32 / vpr) + 1 (exact for numerators below
+// 2^16 and 2 <= vpr <= 2^16; vpr == 1 is handled directly).
+struct RowSplit {
+    uint32_t vpr;
+    uint32_t magic;
+    uint32_t m;
+    uint8_t s1, s2;
+    uint16_t pad;
+};
+
+// One relayout pass, walking every destination vector once (a gather):
+// grid.x takes the destination shards one after another, 64 consecutive
+// vectors of a shard per block; grid.y the batch planes; grid.z the tensors
+// (all of one plan's geometry).  The caller points src and dst at the first
+// batch plane of the launch, so a launch of one plane needs no plane terms.
+//
+// Destination shard r is partitioned among the source ranks: piece (j -> r)
+// covers the destination rows (mode 0) or columns (mode 1) from
+// bound[j] up to bound[j + 1].  The owner of a destination vector at (row,
+// col) is the number of q in [1, world) with bound[q] <= key, key = row in
+// mode 0 and col in mode 1 (an empty piece has bound[j] == bound[j + 1] and
+// is never chosen).  Its source vector within source plane j is
+// off[r][j] + row * pitch[r][j] + col: the piece's source offset, moved to
+// the destination frame's origin (it may be negative).
 struct RelayoutArgs {
     const unsigned char *src[kMaxTensors][kMaxWorld];
     unsigned char *dst[kMaxTensors][kMaxWorld];
-    uint64_t src_plane[kMaxWorld];   // vectors per batch plane of source shard j
-    uint64_t dst_plane[kMaxWorld];   // vectors per batch plane of destination shard r
-    uint32_t blk_begin[kMaxPieces];
-    PieceArgs piece[kMaxPieces];
-    uint32_t src_plane0;             // batch plane of grid.y == 0, source side
-    uint32_t dst_plane0;             // batch plane of grid.y == 0, destination side
-    // Row-band traversal (fill_relayout_bands): the pieces sharing one
-    // row-sharded shard g (source j in mode 0, destination r in mode 1) sit
-    // at piece[g * world + k]; their blocks interleave band by band: block
-    // grp_begin[g] + band * world + k moves rows [band*band_rows,
-    // (band+1)*band_rows) of piece (g, k).  Unused entries hold 0xFFFFFFFF.
-    // With band_vecs != 0 a band is instead band_vecs consecutive vectors of
-    // the piece (the same rows across the group when its rows are equally
-    // wide); a block whose band starts past its piece does nothing.
-    uint32_t grp_begin[kMaxWorld];
-    uint32_t world;
-    uint32_t band_rows;
-    uint32_t band_vecs;
-    // Row-aligned chunk traversal (fill_relayout_aligned; band_vecs == 0 and
-    // chunks_per_band != 0), for groups whose pieces have unequal row widths:
-    // a band is band_rows rows of every piece of the group, cut into chunks
-    // of chunk_vecs vectors (a whole number per piece);
-    // block grp_begin[g] + band * chunks_per_band + q takes chunk
-    // q - chunk_begin[k] of piece (g, k), k being the last piece with
-    // chunk_begin[k] <= q.  band_m/band_s1/band_s2 divide exactly by
-    // chunks_per_band (div32).
-    uint32_t chunk_begin[kMaxWorld + 1];
-    uint32_t chunks_per_band;
-    uint32_t chunk_vecs;
-    uint32_t band_m;
-    uint32_t band_s1, band_s2;
+    uint64_t src_plane[kMaxWorld];          // vectors per batch plane of source shard j
+    uint64_t dst_plane[kMaxWorld];          // vectors per batch plane of destination shard r
+    int64_t off[kMaxWorld][kMaxWorld];      // [r][j]
+    uint32_t pitch[kMaxWorld][kMaxWorld];   // [r][j]
+    uint32_t blk_begin[kMaxWorld];          // first block of destination r; kNone past the world
+    uint32_t nvec[kMaxWorld];               // vectors per plane of destination r
+    RowSplit row[kMaxWorld];                // rows of destination r
+    uint32_t bound[kMaxWorld];              // [0] unused; kNone past the world
+    uint32_t key_col;                       // 0: owner by row (mode 0), 1: by column (mode 1)
 };
 
-// The fused QK-norm + RoPE mode-0 pass: the same piece table for q and k
-// (grid.z picks the tensor), plus the row-op parameters.  Vector counts,
-// offsets and pitches of the pieces are in units of the kernel's vectors per
-// lane (see to_units in the plan).
+// A contiguous copy of nvec[r] vectors per rank, src[r] to dst[r] (one batch
+// plane: the window and the plane the caller points dst at); grid.x takes the
+// ranks one after another, 64 vectors per block.
+struct CopyArgs {
+    const unsigned char *src[kMaxWorld];
+    unsigned char *dst[kMaxWorld];
+    uint32_t blk_begin[kMaxWorld];
+    uint32_t nvec[kMaxWorld];
+};
+
+// The fused QK-norm + RoPE mode-0 pass, walking every source vector once (a
+// scatter): grid.x takes the source shards one after another, kFusedBlock
+// consecutive vectors of a shard per block; grid.y the batch planes (the
+// caller points src and dst at the launch's first plane).  Both q and k move
+// in every block, so the rotary rows a block reads serve both.
+//
+// Source shard j's rows are the full rows of G / 16 = n_global * d / 8
+// vectors (the same split for every j); column col belongs to the
+// destination rank r = the number of q in [1, world) with bound[q] <= col,
+// and lands at off[j][r] + row * pitch[j][r] + col of destination plane r.
+// Source row `row` of shard j sits at global sequence position pos0[j] +
+// row.
 struct FusedArgs {
-    const unsigned char *src[2][kMaxWorld];
+    const unsigned char *src[2][kMaxWorld];   // [0] q, [1] k
     unsigned char *dst[2][kMaxWorld];
     uint64_t src_plane[kMaxWorld];
     uint64_t dst_plane[kMaxWorld];
-    uint32_t blk_begin[kMaxPieces];
-    PieceArgs piece[kMaxPieces];
+    int64_t off[kMaxWorld][kMaxWorld];        // [j][r]
+    uint32_t pitch[kMaxWorld][kMaxWorld];     // [j][r]
+    uint32_t blk_begin[kMaxWorld];            // first block of source j; kNone past the world
+    uint32_t nvec[kMaxWorld];                 // vectors per plane of source j
+    uint32_t pos0[kMaxWorld];
+    uint32_t bound[kMaxWorld];
+    RowSplit row;                             // rows of every source shard
     const float *gamma[2];
     const float *rope_cos;
     const float *rope_sin;
     float eps;
-    float inv_d;                     // 1/d, exact (d is a power of two)
-    uint32_t d;                      // head dimension
-    uint32_t plane0;                 // batch plane of grid.y == 0
-    // band traversal as in RelayoutArgs (band_vecs != 0), else blk_begin
-    uint32_t grp_begin[kMaxWorld];
-    uint32_t world;
-    uint32_t band_vecs;
-    // exact division by world (div32): a block's band within its group
-    uint32_t world_m;
-    uint32_t world_s1, world_s2;
+    float inv_d;                              // 1/d, exact (d is a power of two)
+    uint32_t half_d;                          // d / 2: floats per rotary row
 };
 
 static_assert(sizeof(RelayoutArgs) <= 4096, "kernel argument block over 4 KiB");
+static_assert(sizeof(CopyArgs) <= 4096, "kernel argument block over 4 KiB");
 static_assert(sizeof(FusedArgs) <= 4096, "kernel argument block over 4 KiB");
 
 }  // namespace ulysses

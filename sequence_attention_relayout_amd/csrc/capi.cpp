@@ -18,66 +18,6 @@ struct ulysses_plan {
     ulysses::Plan p;
 };
 
-#ifndef ULY_ORDER
-#define ULY_ORDER 0
-#endif
-// Order in which the pieces of a relayout take consecutive blocks.
-static const ulysses::PieceOrder kRelayoutOrder = static_cast<ulysses::PieceOrder>(ULY_ORDER);
-
-// Launch table choice, by measurement on MI355X (W=8, 75,600 tokens, bf16,
-// GB/s per mode-0 + mode-1 step): bands of 64 vectors on one-wave blocks
-// interleaved over the group (~6.35 TB/s) beat bands of 256 on 128 x 2
-// blocks (~6.15), row bands of ~256 vectors (~6.05) and the flat walk
-// (~5.86).
-#ifndef ULY_BAND
-#define ULY_BAND 0
-#endif
-
-// Launch table of one relayout pass: bands of ULY_VBAND vectors when
-// ULY_VBAND > 0, else row bands of about ULY_BAND vectors when ULY_BAND > 0,
-// else flat blocks in kRelayoutOrder.
-#ifndef ULY_VBAND
-#define ULY_VBAND 64
-#endif
-
-// Row-aligned chunk bands for groups whose pieces differ in width, used when
-// no piece's band holds more than ULY_ALIGNED_MAX_CHUNKS chunks of 64
-// vectors (one chunk per block, piece by piece within a band).  By
-// measurement on MI355X (W=8 or 7, 75,600 tokens, d=128, GB/s per mode):
-// bands of 1-4 chunks per piece gain 5-21% over vector bands, whose bands
-// drift apart in rows (bf16 widths 64/32, 96/64, 128/96; fp32 192/128,
-// 256/192); runs of 5-7 chunks per piece gain up to 7% in mode 1 but lose up
-// to 6% in mode 0 (bf16 80/64, 96/80, 80/48, 224/160; fp32 192/160).
-#ifndef ULY_ALIGNED
-#define ULY_ALIGNED 1
-#endif
-#ifndef ULY_ALIGNED_MAX_CHUNKS
-#define ULY_ALIGNED_MAX_CHUNKS 4
-#endif
-
-// The fused kernel walks bands of one block each when set, else flat blocks
-// in source-major piece order.
-#ifndef ULY_FUSED_BANDS
-#define ULY_FUSED_BANDS 1
-#endif
-static const bool kFusedBands = ULY_FUSED_BANDS != 0;
-
-static uint64_t relayout_table(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs *a) {
-    if (ULY_VBAND > 0) {
-        // pieces of unequal width: bands aligned on rows, one chunk per block
-        if (ULY_ALIGNED) {
-            const uint64_t n = ulysses::fill_relayout_aligned(
-                p, mode, ulysses::relayout_vectors_per_block(), ULY_ALIGNED_MAX_CHUNKS, a);
-            if (n != 0) return n;
-        }
-        return ulysses::fill_relayout_vbands(p, mode, ULY_VBAND, a);
-    }
-    if (ULY_BAND > 0)
-        return ulysses::fill_relayout_bands(p, mode, ulysses::band_rows_for(p, mode, ULY_BAND), a);
-    return ulysses::fill_relayout(p, mode, ulysses::relayout_vectors_per_block(), kRelayoutOrder,
-                                  a);
-}
-
 namespace {
 
 thread_local std::string g_last_error;
@@ -147,16 +87,33 @@ int check_grid(uint64_t grid_x, uint32_t block, const char *what) {
     return ULYSSES_OK;
 }
 
-// A relayout over `planes` batch planes, at most kMaxGridY per launch.
-int launch_planes(ulysses::RelayoutArgs a, uint32_t gx, int64_t planes, uint32_t tensors,
-                  hipStream_t stream, const char *what) {
-    const uint32_t s0 = a.src_plane0, d0 = a.dst_plane0;
-    for (int64_t p0 = 0; p0 < planes; p0 += ulysses::kMaxGridY) {
-        const int64_t n = planes - p0 < ulysses::kMaxGridY ? planes - p0 : ulysses::kMaxGridY;
-        a.src_plane0 = s0 + static_cast<uint32_t>(p0);
-        a.dst_plane0 = d0 + static_cast<uint32_t>(p0);
+// `base` moved forward by `planes` batch planes of `plane_bytes` each (an
+// empty shard keeps its pointer: its planes are 0 bytes).
+template <typename T>
+T *plane_ptr(T *base, int64_t planes, int64_t plane_bytes) {
+    return reinterpret_cast<T *>(reinterpret_cast<uintptr_t>(base) +
+                                 static_cast<uintptr_t>(planes * plane_bytes));
+}
+
+// A relayout over the plan's b batch planes, at most kMaxGridY per launch,
+// each launch's shards pointed at its first plane.
+int launch_planes(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs a, uint32_t gx,
+                  int tensors, const void *const *src, void *const *dst, hipStream_t stream,
+                  const char *what) {
+    const ulysses::ModeGeom &g = p.mode[mode];
+    for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
+        const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
+        for (int t = 0; t < tensors; ++t)
+            for (int r = 0; r < p.world; ++r) {
+                a.src[t][r] = plane_ptr(static_cast<const unsigned char *>(src[t * p.world + r]),
+                                        p0, g.src_plane[r]);
+                a.dst[t][r] = plane_ptr(static_cast<unsigned char *>(dst[t * p.world + r]), p0,
+                                        g.dst_plane[r]);
+            }
         const int rc = launch_status(
-            ulysses::launch_relayout(a, gx, static_cast<uint32_t>(n), tensors, stream), what);
+            ulysses::launch_relayout(a, gx, static_cast<uint32_t>(n), static_cast<uint32_t>(tensors),
+                                     stream),
+            what);
         if (rc) return rc;
     }
     return ULYSSES_OK;
@@ -188,16 +145,6 @@ int check_shards(const ulysses::Plan &p, int mode, const void *const *src, void 
     return ULYSSES_OK;
 }
 
-// Pointers of tensor t: src/dst hold W entries per tensor, tensor-major.
-void set_pointers(const ulysses::Plan &p, int tensors, const void *const *src,
-                  void *const *dst, ulysses::RelayoutArgs *a) {
-    for (int t = 0; t < tensors; ++t)
-        for (int r = 0; r < p.world; ++r) {
-            a->src[t][r] = static_cast<const unsigned char *>(src[t * p.world + r]);
-            a->dst[t][r] = static_cast<unsigned char *>(dst[t * p.world + r]);
-        }
-}
-
 // Validation and launch shared by the one-tensor and multi-tensor calls.
 int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void *const *src,
                      void *const *dst, hipStream_t stream);
@@ -221,12 +168,49 @@ int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void
     rc = check_overlap(ranges);
     if (rc) return rc;
     ulysses::RelayoutArgs a;
-    const uint64_t gx = relayout_table(p, mode, &a);
-    rc = check_grid(gx, ulysses::relayout_block_threads(), "relayout");
+    const uint64_t gx = ulysses::fill_relayout(p, mode, &a);
+    rc = check_grid(gx, ulysses::kRelayoutBlock, "relayout");
     if (rc) return rc;
-    set_pointers(p, tensors, src, dst, &a);
-    return launch_planes(a, static_cast<uint32_t>(gx), p.b, static_cast<uint32_t>(tensors),
-                         stream, "relayout");
+    return launch_planes(p, mode, a, static_cast<uint32_t>(gx), tensors, src, dst, stream,
+                         "relayout");
+}
+
+// The plane-at-a-time passes of a validated call: for each batch plane p,
+// the relayout of plane p into the W windows and a copy of window r into
+// plane p of dst r; with window == nullptr the relayout of plane p writes
+// straight into plane p of the destinations (the window is the output slice).
+int chunked_planes(const ulysses::Plan &p, int mode, const void *const *src, void *const *dst,
+                   const void *const *window, hipStream_t stream) {
+    const ulysses::ModeGeom &g = p.mode[mode];
+    ulysses::RelayoutArgs scatter;
+    ulysses::CopyArgs copy;
+    const uint64_t gs = ulysses::fill_relayout(p, mode, &scatter);
+    const uint64_t gc = ulysses::fill_plane_copy(p, mode, &copy);
+    int rc = check_grid(gs > gc ? gs : gc, ulysses::kRelayoutBlock, "chunked relayout");
+    if (rc) return rc;
+    for (int64_t plane = 0; plane < p.b; ++plane) {
+        for (int r = 0; r < p.world; ++r) {
+            unsigned char *out = plane_ptr(static_cast<unsigned char *>(dst[r]), plane,
+                                           g.dst_plane[r]);
+            scatter.src[0][r] =
+                plane_ptr(static_cast<const unsigned char *>(src[r]), plane, g.src_plane[r]);
+            scatter.dst[0][r] =
+                window ? static_cast<unsigned char *>(const_cast<void *>(window[r])) : out;
+            if (window) {
+                copy.src[r] = static_cast<const unsigned char *>(window[r]);
+                copy.dst[r] = out;
+            }
+        }
+        rc = launch_status(
+            ulysses::launch_relayout(scatter, static_cast<uint32_t>(gs), 1, 1, stream),
+            "plane relayout");
+        if (rc) return rc;
+        if (!window) continue;
+        rc = launch_status(ulysses::launch_plane_copy(copy, static_cast<uint32_t>(gc), stream),
+                           "window copy");
+        if (rc) return rc;
+    }
+    return ULYSSES_OK;
 }
 
 }  // namespace
@@ -315,47 +299,21 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
             return set_error(ULYSSES_EWINDOW, "window bytes per rank per plane " +
                                                   std::to_string(wb) + " exceed the cap " +
                                                   std::to_string(p.window_cap));
-        if (!window) return set_error(ULYSSES_EINVAL, "window array is null");
         std::vector<Range> ranges;
         rc = check_shards(p, mode, src, dst, "src", "dst", &ranges);
         if (rc) return rc;
-        for (int r = 0; r < p.world; ++r) {
-            const std::string wi = "window[" + std::to_string(r) + "]";
-            const int64_t need = p.mode[mode].dst_plane[r];
-            rc = check_ptr(window[r], need, wi);
-            if (rc) return rc;
-            add_range(&ranges, window[r], need, true, wi);
+        if (window) {
+            for (int r = 0; r < p.world; ++r) {
+                const std::string wi = "window[" + std::to_string(r) + "]";
+                const int64_t need = p.mode[mode].dst_plane[r];
+                rc = check_ptr(window[r], need, wi);
+                if (rc) return rc;
+                add_range(&ranges, window[r], need, true, wi);
+            }
         }
         rc = check_overlap(ranges);
         if (rc) return rc;
-
-        ulysses::RelayoutArgs scatter, copy;
-        const uint64_t gs = relayout_table(p, mode, &scatter);
-        const uint64_t gc =
-            ulysses::fill_window_copy(p, mode, ulysses::relayout_vectors_per_block(), &copy);
-        rc = check_grid(gs > gc ? gs : gc, ulysses::relayout_block_threads(), "chunked relayout");
-        if (rc) return rc;
-        for (int r = 0; r < p.world; ++r) {
-            scatter.src[0][r] = static_cast<const unsigned char *>(src[r]);
-            scatter.dst[0][r] = static_cast<unsigned char *>(window[r]);
-            copy.src[0][r] = static_cast<const unsigned char *>(window[r]);
-            copy.dst[0][r] = static_cast<unsigned char *>(dst[r]);
-        }
-        for (int64_t plane = 0; plane < p.b; ++plane) {
-            scatter.src_plane0 = static_cast<uint32_t>(plane);
-            scatter.dst_plane0 = 0;
-            rc = launch_status(
-                ulysses::launch_relayout(scatter, static_cast<uint32_t>(gs), 1, 1, stream),
-                "chunk relayout");
-            if (rc) return rc;
-            copy.src_plane0 = 0;
-            copy.dst_plane0 = static_cast<uint32_t>(plane);
-            rc = launch_status(
-                ulysses::launch_relayout(copy, static_cast<uint32_t>(gc), 1, 1, stream),
-                "window copy");
-            if (rc) return rc;
-        }
-        return ULYSSES_OK;
+        return chunked_planes(p, mode, src, dst, window, stream);
     });
 }
 
@@ -393,51 +351,28 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         rc = check_overlap(ranges);
         if (rc) return rc;
 
-        // d = 128: the band kernel, bands of `bv` 16-byte vectors; other d:
-        // fused_kernel, one lane moving `vpl` consecutive vectors of a head row
-        const uint32_t bv = ulysses::fused_band_vectors(static_cast<uint32_t>(p.d));
-        const uint32_t vpl =
-            bv != 0 ? 1 : ulysses::fused_vectors_per_lane(static_cast<uint32_t>(p.d));
-        const uint32_t upb = ulysses::fused_units_per_block();
-        ulysses::RelayoutArgs t;
-        const uint64_t gx =
-            bv != 0       ? ulysses::fill_relayout_vbands(p, 0, bv, &t)
-            : kFusedBands ? ulysses::fill_relayout_vbands(p, 0, upb * vpl, &t)
-                          : ulysses::fill_relayout(p, 0, upb * vpl, ulysses::kSrcMajor, &t);
-        if (!ulysses::to_units(&t, vpl))
-            return set_error(ULYSSES_EINVAL, "fused launch table not divisible into lane units");
         ulysses::FusedArgs a;
-        std::memset(&a, 0, sizeof a);
-        for (int r = 0; r < p.world; ++r) {
-            a.src[0][r] = static_cast<const unsigned char *>(q_src[r]);
-            a.dst[0][r] = static_cast<unsigned char *>(q_dst[r]);
-            a.src[1][r] = static_cast<const unsigned char *>(k_src[r]);
-            a.dst[1][r] = static_cast<unsigned char *>(k_dst[r]);
-            a.src_plane[r] = t.src_plane[r];
-            a.dst_plane[r] = t.dst_plane[r];
-        }
-        std::memcpy(a.blk_begin, t.blk_begin, sizeof a.blk_begin);
-        std::memcpy(a.piece, t.piece, sizeof a.piece);
-        std::memcpy(a.grp_begin, t.grp_begin, sizeof a.grp_begin);
-        a.world = t.world;
-        a.band_vecs = t.band_vecs;
-        const ulysses::Div32Magic wm = ulysses::div32_magic(t.world > 0 ? t.world : 1);
-        a.world_m = wm.m;
-        a.world_s1 = wm.s1;
-        a.world_s2 = wm.s2;
+        const uint64_t gx = ulysses::fill_fused(p, &a);
+        rc = check_grid(gx, ulysses::kFusedBlock, "fused relayout");
+        if (rc) return rc;
         a.gamma[0] = gamma_q;
         a.gamma[1] = gamma_k;
         a.rope_cos = rope_cos;
         a.rope_sin = rope_sin;
         a.eps = eps;
-        a.inv_d = 1.0f / static_cast<float>(p.d);   // exact: d is a power of two
-        a.d = static_cast<uint32_t>(p.d);
-        rc = check_grid(gx, ulysses::fused_block_threads(a.d), "fused relayout");
-        if (rc) return rc;
+        const ulysses::ModeGeom &g = p.mode[0];
         for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
             const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
-            a.plane0 = static_cast<uint32_t>(p0);
-            rc = launch_status(ulysses::launch_fused(a, static_cast<uint32_t>(gx),
+            for (int r = 0; r < p.world; ++r) {
+                a.src[0][r] =
+                    plane_ptr(static_cast<const unsigned char *>(q_src[r]), p0, g.src_plane[r]);
+                a.dst[0][r] = plane_ptr(static_cast<unsigned char *>(q_dst[r]), p0, g.dst_plane[r]);
+                a.src[1][r] =
+                    plane_ptr(static_cast<const unsigned char *>(k_src[r]), p0, g.src_plane[r]);
+                a.dst[1][r] = plane_ptr(static_cast<unsigned char *>(k_dst[r]), p0, g.dst_plane[r]);
+            }
+            rc = launch_status(ulysses::launch_fused(a, static_cast<uint32_t>(p.d),
+                                                     static_cast<uint32_t>(gx),
                                                      static_cast<uint32_t>(n), stream),
                                "fused relayout");
             if (rc) return rc;

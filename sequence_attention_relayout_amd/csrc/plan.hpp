@@ -1,6 +1,6 @@
 // Host-side plan of the Ulysses 4D relayout: validation, offsets, the piece
-// table and launch tables.  No HIP headers: it builds and is tested on a
-// machine without a GPU.
+// table and the kernels' launch tables.  No HIP headers: it builds and is
+// tested on a machine without a GPU.
 //
 // The addressing follows the pages' description of the exchange as pitched
 // copies whose source and destination strides perform the sequence/head
@@ -29,25 +29,30 @@ enum Status : int {
 // Bytes per element of an ulysses_dtype value, or -1 if unknown.
 int64_t dtype_size(int dtype);
 
-// One (j -> r) region of a batch plane, in bytes.
+// One (j -> r) region of a batch plane, in bytes: `rows` rows of `row_bytes`
+// contiguous bytes on both sides.  Its first byte is at src_off within
+// source plane j and at dst_off within destination plane r, consecutive rows
+// src_pitch and dst_pitch apart.  In the frame of each shard (rows of its
+// own pitch) the region is the rectangle of rows from *_row0 and bytes from
+// *_col0, so *_off = *_row0 * *_pitch + *_col0.
 struct Piece {
     int j = 0, r = 0;
-    int64_t rows = 0;        // rows of the region
-    int64_t row_bytes = 0;   // contiguous bytes per row (same on both sides)
-    int64_t src_off = 0;     // byte offset of the first row within source plane j
-    int64_t dst_off = 0;     // byte offset of the first row within destination plane r
-    int64_t src_pitch = 0;   // bytes between consecutive source rows
-    int64_t dst_pitch = 0;   // bytes between consecutive destination rows
+    int64_t rows = 0;
+    int64_t row_bytes = 0;
+    int64_t src_off = 0, dst_off = 0;
+    int64_t src_pitch = 0, dst_pitch = 0;
+    int64_t src_row0 = 0, src_col0 = 0;
+    int64_t dst_row0 = 0, dst_col0 = 0;
     int64_t seq_pos0 = 0;    // global sequence position of the region's first row
 };
 
 struct ModeGeom {
-    Piece piece[kMaxPieces];            // index j * world + r
-    int64_t src_plane[kMaxWorld] = {};  // bytes per batch plane, source shard j
-    int64_t dst_plane[kMaxWorld] = {};  // bytes per batch plane, destination shard r
+    Piece piece[kMaxWorld * kMaxWorld];   // index j * world + r
+    int64_t src_plane[kMaxWorld] = {};    // bytes per batch plane, source shard j
+    int64_t dst_plane[kMaxWorld] = {};    // bytes per batch plane, destination shard r
     int64_t src_shape[kMaxWorld][4] = {};
     int64_t dst_shape[kMaxWorld][4] = {};
-    int64_t window_bytes = 0;           // max_r dst_plane[r]
+    int64_t window_bytes = 0;             // max_r dst_plane[r]
 };
 
 struct Plan {
@@ -68,56 +73,25 @@ struct Plan {
 int plan_build(Plan *p, int world, int64_t b, int64_t d, const int64_t *seq_splits,
                const int64_t *head_splits, int dtype, int64_t window_cap, std::string *msg);
 
-// Order in which pieces take consecutive blocks of the grid.
-enum PieceOrder : int {
-    kDstMajor = 0,   // for r: for j   (destination shards filled one after another)
-    kSrcMajor = 1,   // for j: for r   (source shards drained one after another)
-};
+// Launch table of one relayout pass of `mode` (the gather of RelayoutArgs).
+// Pointers are left to the caller.  Returns the number of blocks along grid.x
+// (0 when nothing moves) as a 64-bit count that the caller checks against the
+// launch limits.
+uint64_t fill_relayout(const Plan &p, int mode, RelayoutArgs *a);
 
-// Launch table of one relayout pass of `mode` with `vec_per_block` 16-byte
-// vectors per block.  Pointers and plane bases are left to the caller.
-// Returns the number of blocks along grid.x (0 when nothing moves), as a
-// 64-bit count: the caller checks it against the launch limits before use.
-uint64_t fill_relayout(const Plan &p, int mode, uint32_t vec_per_block, PieceOrder order,
-                       RelayoutArgs *a);
+// Launch table of the copy of one batch plane from each of the W windows
+// into the destination shards of `mode` (CopyArgs).  Returns grid.x.
+uint64_t fill_plane_copy(const Plan &p, int mode, CopyArgs *a);
 
-// Row-band launch table of one relayout pass of `mode` (see
-// RelayoutArgs::grp_begin): bands of `band_rows` rows.  Returns grid.x.
-uint64_t fill_relayout_bands(const Plan &p, int mode, uint32_t band_rows, RelayoutArgs *a);
+// Launch table of the fused mode-0 scatter (FusedArgs) with kFusedBlock
+// vectors per block; pointers, gains, tables and eps are left to the caller.
+// Returns grid.x.
+uint64_t fill_fused(const Plan &p, FusedArgs *a);
 
-// Vector-band launch table: bands of `band_vecs` vectors of each piece,
-// interleaved over the group as for row bands.  Returns grid.x.
-uint64_t fill_relayout_vbands(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
-
-// Row-aligned chunk table (see RelayoutArgs::chunk_begin) when the pieces of
-// a group differ in row width: bands of R rows, R the fewest rows that make
-// every piece's band a whole number of chunk_vecs-vector chunks, one chunk
-// per block, so blocks running side by side cover the same rows of every
-// piece.  Returns grid.x, or 0 without touching *a when the pieces of a group
-// all have the same width, or when max_chunks != 0 and some piece's band
-// would hold more than max_chunks chunks (then fill_relayout_vbands applies).
-uint64_t fill_relayout_aligned(const Plan &p, int mode, uint32_t chunk_vecs, uint32_t max_chunks,
-                               RelayoutArgs *a);
-
-// Band height so that one band of the widest piece moves about
-// `target_vectors` 16-byte vectors (at least one row).
-uint32_t band_rows_for(const Plan &p, int mode, uint32_t target_vectors);
-
-// Launch table of the plane copy from the W windows (one destination plane
-// each) into the destination shards, for the band kernel: group r holds the
-// one piece copying window r (equal row pitches on both sides), in bands of
-// `band_vecs` vectors.
-uint64_t fill_window_copy(const Plan &p, int mode, uint32_t band_vecs, RelayoutArgs *a);
-
-// Rescales a launch table from 16-byte vectors to units of `vpl` vectors
-// (vector counts, offsets, pitches, plane sizes and band width divided by
-// vpl, magic multipliers recomputed); block ranges are unchanged, so the
-// table must have been filled with vec_per_block (or band_vecs) = units per
-// block * vpl.  Returns
-// false, leaving *a unusable, if any count is not a multiple of vpl.
-bool to_units(RelayoutArgs *a, uint32_t vpl);
-
-// Magic multiplier for the kernels' division by vpr (see PieceArgs::magic).
+// Magic multiplier of the kernels' lane division by vpr (see RowSplit).
 uint32_t row_magic(uint32_t vpr);
+
+// The full row split of vpr vectors per row (vpr >= 1).
+RowSplit row_split(uint32_t vpr);
 
 }  // namespace ulysses

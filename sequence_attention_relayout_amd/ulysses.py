@@ -246,15 +246,16 @@ def _check_len(items, world, what):
     return items
 
 
-def ulysses_a2a_4d_chunked(plan, mode, src, dst, window, stream=None):
+def ulysses_a2a_4d_chunked(plan, mode, src, dst, window=None, stream=None):
     """window: W device buffers, window r holding one batch plane of
-    destination r (ulysses_plan_window_bytes is enough for every rank)."""
+    destination r (ulysses_plan_window_bytes is enough for every rank), or
+    None: each plane is relayed straight into its place in dst (no copy-out)."""
     w = plan.world
     planes = [n // plan.b for n in plan.shard_bytes(mode, True)]
+    win = None if window is None else _ptr_array(window, w, "window", planes)
     _check(_load().ulysses_a2a_4d_chunked(
         plan.handle, int(mode), _ptr_array(src, w, "src", plan.shard_bytes(mode, False)),
-        _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)),
-        _ptr_array(window, w, "window", planes), _stream(stream)))
+        _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)), win, _stream(stream)))
 
 
 def ulysses_a2a_4d_qknorm_rope(plan, q_src, q_dst, k_src, k_dst, gamma_q, gamma_k, eps,

@@ -2,11 +2,11 @@
 
 Bar: bit-exact bytes for the pure relayout in every dtype; for the fused
 QK RMSNorm + RoPE path at most 1 bf16 ulp (ordinal distance) from the
-oracle, every element.  Medium sizes (several blocks per piece, ragged
-tails) compare every element; the full workload sizes compare sampled
-outputs the oracle computes one by one (plus every element of the rows at
-rank boundaries) and check the round trip on the device.  Destination
-shards sit between guard bands and are pre-filled with poison.
+oracle, every element.  Every element is compared, at medium sizes (several
+blocks per shard, ragged tails) and at the full sizes of the timed
+workloads (the oracle's threaded loops on the host's cores); only the
+shards beyond 4 GiB are checked on sampled elements.  Destination shards
+sit between guard bands and are pre-filled with poison.
 """
 import os
 
@@ -23,6 +23,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 EPS = 1e-6
 THETA = 10000.0
+# host threads for the oracle at full sizes (the same loops; identical results)
+NT = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -52,8 +54,8 @@ def run_relayout(plan, mode, srcs, dtype_name):
     return out
 
 
-def check_full(mode, b, d, seq, head, srcs, outs):
-    want = oracle.a2a_4d(mode, b, d, seq, head, [H.to_np(x) for x in srcs])
+def check_full(mode, b, d, seq, head, srcs, outs, threads=1):
+    want = oracle.a2a_4d(mode, b, d, seq, head, [H.to_np(x) for x in srcs], threads=threads)
     for r, (g, w) in enumerate(zip(outs, want)):
         got = H.to_np(g)
         assert got.shape == w.shape
@@ -74,15 +76,6 @@ def boundary_rows(mode, b, seq, head):
                 cand = {0, seq[r] - 1} if seq[r] > 0 else set()
             rows += [(r, bi, c) for c in sorted(cand)]
     return rows
-
-
-def check_sampled(mode, b, d, seq, head, srcs_host, outs, rng, n=400_000):
-    shapes = [tuple(o.shape) for o in outs]
-    coords = H.sample_coords(rng, shapes, n, boundary_rows(mode, b, seq, head))
-    want = oracle.a2a_4d_sample(mode, b, d, seq, head, srcs_host, coords)
-    got = H.gather([H.to_np(o) for o in outs], coords)
-    bad = np.count_nonzero(got != want)
-    assert bad == 0, f"mode {mode}: {bad} of {len(coords)} sampled elements differ"
 
 
 # ---------------------------------------------------------------------------
@@ -152,13 +145,12 @@ def test_random_geometries_every_dtype(seed):
 
 def test_many_tiny_random_geometries():
     """300 tiny random geometries in one process (W 1-8, splits 0-40 with
-    zeros, head counts 0-12, b 1-3, every dtype and several row widths; a
-    third of them with head counts in multiples of 4 so that unequal widths
-    take the row-aligned walk): both modes, two tensors in one launch, the
-    plane-at-a-time call, and the fused call for bf16, every element against
-    the oracle."""
+    zeros, head counts 0-12, b 1-3, every dtype and several row widths, a
+    third of them with head counts in multiples of 4): both modes, two
+    tensors in one launch, the plane-at-a-time call through windows and
+    straight into the destination, and the fused call for bf16, every
+    element against the oracle."""
     rng = np.random.default_rng(9000)
-    aligned = 0
     for case in range(300):
         dt = W.DTYPES[int(rng.integers(0, len(W.DTYPES)))]
         esz = W.ELEM_BYTES[dt]
@@ -167,15 +159,12 @@ def test_many_tiny_random_geometries():
         d = (16 // esz) * int(rng.choice([1, 2, 4, 8]))
         seq = [int(v) for v in rng.integers(0, 41, world)]
         head = [int(v) for v in rng.integers(0, 10, world)]
-        if case % 3 == 0:   # widths of whole multiples of 32 vectors: row-aligned bands
+        if case % 3 == 0:   # row widths in whole multiples of 32 vectors
             d = (16 // esz) * 8
             head = [4 * int(v) for v in rng.integers(0, 4, world)]
         seq[int(rng.integers(0, world))] += 1
         if sum(head) == 0:
             head[int(rng.integers(0, world))] += 4
-        widths = {h * d * esz // 16 for h in head if h}
-        rows = 64 // int(np.gcd(64, int(np.gcd.reduce(list(widths)))))
-        aligned += len(widths) > 1 and rows * max(widths) <= 4 * 64
         plan = U.ulysses_plan_create(world, b, d, seq, head, dt, 1 << 30)
         wl = W.Workload("tiny random", world, b, d, seq, head)
         for mode in (0, 1):
@@ -203,6 +192,10 @@ def test_many_tiny_random_geometries():
                 U.ulysses_a2a_4d_chunked(plan, 1, xs, cout, win)
                 torch.cuda.synchronize()
                 check_full(1, b, d, seq, head, xs, cout)
+                direct = [torch.empty_like(t) for t in cout]
+                U.ulysses_a2a_4d_chunked(plan, 1, xs, direct, None)
+                torch.cuda.synchronize()
+                check_full(1, b, d, seq, head, xs, direct)
         if dt == "bf16" and (d // 8) & (d // 8 - 1) == 0:
             qs = W.make_shards(wl, 0, "bf16", 9700 + case, DEV)
             ks = W.make_shards(wl, 0, "bf16", 9800 + case, DEV)
@@ -215,18 +208,16 @@ def test_many_tiny_random_geometries():
                 for o, w in zip(out, want):
                     hist = ulp_hist(H.to_np(o), w)
                     assert hist[2] == 0 and hist[3] == 0, f"fused case {case}"
-    H.say(f"  300 cases, {aligned} walked in row-aligned chunks")
-    assert aligned > 30
+    H.say("  300 cases")
 
 
 @pytest.mark.parametrize("head", [[6, 6, 6, 6, 4, 4, 4, 4], [4, 4, 4, 4, 2, 2, 2, 2],
                                   [8, 8, 4, 4], [4, 2, 0, 2, 6]])
-def test_unequal_head_widths_row_aligned(head):
-    """Head splits whose rows differ in width and whose bands of whole
-    64-vector chunks hold at most four chunks per piece: the relayout walks
-    row-aligned chunks (one band of every piece covers the same rows).
-    Uneven sequence splits, two batch planes, every element compared in both
-    modes."""
+def test_unequal_head_widths(head):
+    """Head splits whose rows differ in width (and a rank without heads):
+    destination rows of different lengths in mode 0, pieces of different
+    widths within one destination row in mode 1.  Uneven sequence splits,
+    two batch planes, every element compared in both modes."""
     world = len(head)
     seq = W.seeded_partition(11, 2001 * world, world)
     H.say(f"case: unequal head widths W={world} seq={seq} head={head}")
@@ -239,10 +230,10 @@ def test_unequal_head_widths_row_aligned(head):
 
 @pytest.mark.parametrize("seed", range(12))
 def test_random_medium_geometries(seed):
-    """Larger random geometries (up to ~48 MB per tensor): many bands per
-    piece, long and short rows, uneven and zero splits, every dtype; every
+    """Larger random geometries (up to ~48 MB per tensor): many blocks per
+    shard, long and short rows, uneven and zero splits, every dtype; every
     element compared in both modes, plus the fused path for bf16 with
-    d = 128 (band kernel) or another d (generic kernel)."""
+    d = 128, 64 or 256."""
     rng = np.random.default_rng(7000 + seed)
     dt = W.DTYPES[seed % len(W.DTYPES)]
     esz = W.ELEM_BYTES[dt]
@@ -303,23 +294,23 @@ def test_w8_medium_full_compare():
 
 
 def test_w8_wan720p_full_size():
+    """The timed geometry: every element of both modes against the oracle,
+    and the round trip."""
     wl = W.workloads()["w8_wan720p"]
-    H.say(f"case: {wl.name} (sampled + round trip)")
+    H.say(f"case: {wl.name} (every element)")
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
-    rng = np.random.default_rng(22)
     xs = W.make_shards(wl, 0, "bf16", wl.seed, DEV)
     ys = run_relayout(plan, 0, xs, "bf16").views
     for y in ys:
         assert tuple(y.shape) == (1, 75600, 5, 128)
-    check_sampled(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in xs], ys,
-                  rng)
+    check_full(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, xs, ys, threads=NT)
     zs = run_relayout(plan, 1, ys, "bf16").views
     for x, z in zip(xs, zs):
         assert torch.equal(x.view(torch.int16), z.view(torch.int16))
+    del ys, zs
     fresh = W.make_shards(wl, 1, "bf16", wl.seed + 1, DEV)
     outs = run_relayout(plan, 1, fresh, "bf16").views
-    check_sampled(1, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in fresh],
-                  outs, rng)
+    check_full(1, wl.b, wl.d, wl.seq_splits, wl.head_splits, fresh, outs, threads=NT)
 
 
 # ---------------------------------------------------------------------------
@@ -340,15 +331,15 @@ def test_w7_uneven_medium_full_compare(dt):
 
 @pytest.mark.parametrize("dt", ["bf16", "fp32", "fp8_e4m3", "int8"])
 def test_w7_uneven_full_size(dt):
+    """The uneven W=7 workload in each of its dtypes: every element of both
+    modes against the oracle, and the round trip."""
     wl = W.workloads()["w7_uneven"]
-    H.say(f"case: {wl.name} dtype={dt} seq={wl.seq_splits}")
+    H.say(f"case: {wl.name} dtype={dt} seq={wl.seq_splits} (every element)")
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, dt)
-    rng = np.random.default_rng(33)
     for mode in (0, 1):
         xs = W.make_shards(wl, mode, dt, 40 + mode, DEV)
         outs = run_relayout(plan, mode, xs, dt).views
-        check_sampled(mode, wl.b, wl.d, wl.seq_splits, wl.head_splits,
-                      [H.to_np(x) for x in xs], outs, rng, n=200_000)
+        check_full(mode, wl.b, wl.d, wl.seq_splits, wl.head_splits, xs, outs, threads=NT)
         back = run_relayout(plan, 1 - mode, outs, dt).views
         for x, z in zip(xs, back):
             assert torch.equal(bits(x), bits(z))
@@ -380,22 +371,18 @@ def test_multi_tensor_equals_oracle(ntensors, dt, world):
 
 
 def test_w8_qkv_multi_full_size():
-    """q, k, v of the timed geometry in one launch equal three single calls."""
+    """q, k, v of the timed geometry in one launch: every element of each
+    against the oracle."""
     wl = W.workloads()["w8_wan720p"]
-    H.say("case: w8 75.6k q, k, v in one launch")
+    H.say("case: w8 75.6k q, k, v in one launch (every element)")
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
     xs = [W.make_shards(wl, 0, "bf16", 130 + t, DEV) for t in range(3)]
-    multi = [[torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in dst_shapes(plan, 0)]
-             for _ in range(3)]
-    U.ulysses_a2a_4d_multi(plan, 0, xs, multi)
-    single = [run_relayout(plan, 0, x, "bf16").views for x in xs]
+    multi = [H.Guarded(dst_shapes(plan, 0), "bf16", DEV) for _ in range(3)]
+    U.ulysses_a2a_4d_multi(plan, 0, xs, [m.views for m in multi])
     torch.cuda.synchronize()
-    for m, sgl in zip(multi, single):
-        for a, b_ in zip(m, sgl):
-            assert torch.equal(bits(a), bits(b_))
-    rng = np.random.default_rng(131)
-    check_sampled(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in xs[2]],
-                  multi[2], rng, n=100_000)
+    for x, m in zip(xs, multi):
+        assert m.guards_intact()
+        check_full(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, x, m.views, threads=NT)
 
 
 # ---------------------------------------------------------------------------
@@ -455,6 +442,11 @@ def test_chunked_medium_full_compare():
         torch.cuda.synchronize()
         assert out.guards_intact()
         check_full(mode, 3, 128, seq, head, xs, out.views)
+        direct = H.Guarded(dst_shapes(plan, mode), "bf16", DEV)
+        U.ulysses_a2a_4d_chunked(plan, mode, xs, direct.views, None)
+        torch.cuda.synchronize()
+        assert direct.guards_intact()
+        check_full(mode, 3, 128, seq, head, xs, direct.views)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -483,11 +475,33 @@ def test_random_chunked_every_dtype(seed):
         torch.cuda.synchronize()
         assert out.guards_intact()
         check_full(mode, b, d, seq, head, xs, out.views)
+        direct = H.Guarded(dst_shapes(plan, mode), dt, DEV)
+        U.ulysses_a2a_4d_chunked(plan, mode, xs, direct.views, None)
+        torch.cuda.synchronize()
+        assert direct.guards_intact()
+        check_full(mode, b, d, seq, head, xs, direct.views)
+
+
+def check_planes(mode, wl, srcs_host, outs):
+    """Every element of a batch-plane pack, one plane at a time against the
+    oracle (each plane is an independent relayout of batch 1)."""
+    outs_host = [H.to_np(o) for o in outs]
+    for p in range(wl.b):
+        want = oracle.a2a_4d(mode, 1, wl.d, wl.seq_splits, wl.head_splits,
+                             [x[p:p + 1] for x in srcs_host], threads=NT)
+        for r, (o, w) in enumerate(zip(outs_host, want)):
+            bad = np.count_nonzero(o[p:p + 1] != w)
+            assert bad == 0, f"mode {mode} plane {p} rank {r}: {bad} elements differ"
 
 
 def test_w4_qkv_chunked_full_size(golden):
+    """The FastVideo geometry (Q, K, V packed as three batch planes, 1 GiB
+    window cap): the plane-at-a-time call through the windows, every element
+    of every plane against the oracle; the same call writing straight into
+    the destination, and the one-pass relayout, equal to it; the mode-1 call
+    returns the input."""
     wl = W.workloads()["w4_qkv_chunked"]
-    H.say(f"case: {wl.name}")
+    H.say(f"case: {wl.name} (every element)")
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16",
                                  wl.window_cap_bytes)
     assert U.ulysses_plan_window_bytes(plan, 0) == golden["fastvideo_window"]["bytes_per_plane"]
@@ -496,17 +510,19 @@ def test_w4_qkv_chunked_full_size(golden):
     ys = [torch.empty(s, dtype=torch.bfloat16, device=DEV) for s in dst_shapes(plan, 0)]
     U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(44)
-    check_sampled(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in xs], ys,
-                  rng, n=300_000)
-    # the window is invisible in the result: equal to the one-pass relayout
-    direct = [torch.empty_like(y) for y in ys]
-    U.ulysses_a2a_4d(plan, 0, xs, direct)
-    torch.cuda.synchronize()
-    for y, t in zip(ys, direct):
-        assert torch.equal(y.view(torch.int16), t.view(torch.int16))
-    del direct
-    torch.cuda.empty_cache()
+    del win
+    check_planes(0, wl, [H.to_np(x) for x in xs], ys)
+    # the window is invisible in the result: straight into the destination
+    # and the one-pass relayout give the same bytes
+    for direct_call in (lambda out: U.ulysses_a2a_4d_chunked(plan, 0, xs, out, None),
+                        lambda out: U.ulysses_a2a_4d(plan, 0, xs, out)):
+        direct = [torch.empty_like(y) for y in ys]
+        direct_call(direct)
+        torch.cuda.synchronize()
+        for y, t in zip(ys, direct):
+            assert torch.equal(y.view(torch.int16), t.view(torch.int16))
+        del direct
+        torch.cuda.empty_cache()
     zs = [torch.empty_like(x) for x in xs]
     U.ulysses_a2a_4d_chunked(plan, 1, ys, zs, windows(plan, 1))
     torch.cuda.synchronize()
@@ -569,9 +585,9 @@ def test_fused_medium_full_compare(d, world, seq_total):
 
 @pytest.mark.parametrize("world,heads", [(2, [12, 9]), (1, [20]), (3, [17, 0, 8])])
 def test_fused_many_heads_full_compare(world, heads):
-    """Many heads per rank (and a rank with none): with d = 128 a band of
-    the fused band kernel spans several head rows of a piece row, or several
-    piece rows when the rank has few heads."""
+    """Many heads per rank (and a rank with none): with d = 128 a block of
+    the fused scatter spans head rows of several destination ranks, or
+    several source rows when the rows are short."""
     seq = W.seeded_partition(7, 300, world) if world > 1 else [300]
     H.say(f"case: fused many heads W={world} seq={seq} head={heads}")
     plan = U.ulysses_plan_create(world, 2, 128, seq, heads, "bf16")
@@ -626,6 +642,58 @@ def test_fused_sum_order_reaches_the_output(d):
         assert np.array_equal(H.to_np(o), want)
 
 
+def run_one_row(d, x, gamma, cos_row, sin_row, eps):
+    """One bf16 row (W = 1, b = 1, one head, position 0) through the fused
+    call with an explicit one-row rotary table; returns (gpu bits, oracle
+    bits)."""
+    row = np.zeros(d)
+    row[:len(x)] = x
+    xt = torch.tensor(row, dtype=torch.float32).to(torch.bfloat16).reshape(1, 1, 1, d)
+    g = np.ones(d, np.float32)
+    g[:len(gamma)] = gamma
+    c = np.ones((1, d // 2), np.float32)
+    s_ = np.zeros((1, d // 2), np.float32)
+    c[0, :len(cos_row)] = cos_row
+    s_[0, :len(sin_row)] = sin_row
+    plan = U.ulysses_plan_create(1, 1, d, [1], [1], "bf16")
+    gd = torch.from_numpy(g).to(DEV)
+    tab = (torch.from_numpy(c).to(DEV), torch.from_numpy(s_).to(DEV))
+    qo = H.Guarded(dst_shapes(plan, 0), "bf16", DEV)
+    ko = H.Guarded(dst_shapes(plan, 0), "bf16", DEV)
+    U.ulysses_a2a_4d_qknorm_rope(plan, [xt.to(DEV)], qo.views, [xt.to(DEV)], ko.views, gd, gd,
+                                 eps, tab[0], tab[1])
+    torch.cuda.synchronize()
+    assert qo.guards_intact() and ko.guards_intact()
+    want = oracle.qknorm_rope_mode0(1, d, [1], [1], [H.to_np(xt)], g, eps, c, s_)[0].reshape(d)
+    got_q, got_k = H.to_np(qo.views[0]).reshape(d), H.to_np(ko.views[0]).reshape(d)
+    assert np.array_equal(got_q, got_k)
+    return got_q, want
+
+
+@pytest.mark.parametrize("d", [8, 128])
+def test_fused_rounding_rows_reach_the_output(d):
+    """The rows that pin the fused row's rounding steps on the CPU, through
+    the GPU: four rotation pairs whose outputs change if any product is
+    contracted into its add or subtract (expected bf16 0, 2, 0, 2, -2, 0,
+    -2, 0), and one element whose output changes if the gain is folded into
+    inv first (0x4061 at d = 8, 0x415E at d = 128, worked out by hand in
+    exact arithmetic on the CPU).  The GPU must give the oracle's bits."""
+    H.say(f"case: fused rounding rows d={d}")
+    e11, e12 = 2.0 ** -11, 2.0 ** -12
+    x = [0.5] * 8 + ([4.0, 3.0, 2.0, 1.0] if d == 128 else [])
+    gamma = [1 + e12, 1, 1, 1 + e12, 1 + e12, 1, 1, 1 + e12]
+    cos_row = [1 + e12, 1 + e11, -(1 + e11), -(1 + e12)]
+    sin_row = [1 + e11, 1 + e12, 1 + e12, 1 + e11]
+    got, want = run_one_row(d, x, gamma, cos_row, sin_row, 0.0)
+    assert [int(v) for v in want[:8]] == [0x0000, 0x4000, 0x0000, 0x4000,
+                                          0xC000, 0x0000, 0xC000, 0x0000]
+    assert np.array_equal(got, want)
+    g0 = float(np.uint32({8: 0x3F9EBED7, 128: 0x3F9D54CD}[d]).view(np.float32))
+    got, want = run_one_row(d, [1.5], [g0], [], [], 0.0)
+    assert int(want[0]) == {8: 0x4061, 128: 0x415E}[d]
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("seed", range(10))
 def test_random_fused(seed):
     rng = np.random.default_rng(4000 + seed)
@@ -655,38 +723,32 @@ def test_random_fused(seed):
 
 
 def test_w8_fused_full_size():
+    """The fused workload: every element of q and k against the oracle's
+    fused row operation (at most 1 bf16 ulp; the histogram is reported), and
+    every element of v through the plain relayout."""
     wl = W.workloads()["w8_fused_qknorm_rope"]
-    H.say(f"case: {wl.name} (sampled rows)")
+    H.say(f"case: {wl.name} (every element)")
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
     qs = W.make_shards(wl, 0, "bf16", 70, DEV)
     ks = W.make_shards(wl, 0, "bf16", 71, DEV)
-    vs = W.make_shards(wl, 0, "bf16", 72, DEV)
     gq, gk = W.make_gamma(wl.d, 73, DEV), W.make_gamma(wl.d, 74, DEV)
     tab, (oc, osn) = rope_tables(wl.s_global, wl.d)
     qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
-    vo = run_relayout(plan, 0, vs, "bf16").views
-    rng = np.random.default_rng(75)
-    so = np.cumsum([0] + wl.seq_splits)
-    rows = []
-    for r in range(wl.world):
-        picks = set(int(v) for v in rng.integers(0, wl.s_global, 2500))
-        picks |= {int(v) for o in so[1:-1] for v in (o - 1, o)} | {0, wl.s_global - 1}
-        rows += [(r, 0, S, h) for S in sorted(picks) for h in range(wl.head_splits[r])]
-    rows = np.array(rows, dtype=np.int64)
     for name, src, out, g in (("q", qs, qo, gq), ("k", ks, ko, gk)):
-        host = [H.to_np(x) for x in src]
-        want = oracle.qknorm_rope_mode0_sample(wl.b, wl.d, wl.seq_splits, wl.head_splits, host,
-                                               g.cpu().numpy(), EPS, oc, osn, rows)
-        outs = [H.to_np(o) for o in out]
-        got = np.empty((len(rows), wl.d), dtype=np.uint16)
-        for r in range(wl.world):
-            sel = rows[:, 0] == r
-            got[sel] = outs[r][rows[sel, 1], rows[sel, 2], rows[sel, 3]]
-        hist = ulp_hist(got, want)
-        H.say(f"  {name}: {len(rows)} rows, ulp histogram (0,1,2,>=3): {hist.tolist()}")
+        want = oracle.qknorm_rope_mode0(wl.b, wl.d, wl.seq_splits, wl.head_splits,
+                                        [H.to_np(x) for x in src], g.cpu().numpy(), EPS, oc, osn,
+                                        threads=NT)
+        hist = np.zeros(4, np.int64)
+        for o, w in zip(out, want):
+            hist += ulp_hist(H.to_np(o), w)
+        H.say(f"  {name}: ulp histogram (0,1,2,>=3): {hist.tolist()}")
         assert hist[2] == 0 and hist[3] == 0
-    check_sampled(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, [H.to_np(x) for x in vs], vo,
-                  rng, n=200_000)
+        del want
+    del qs, ks, qo, ko
+    torch.cuda.empty_cache()
+    vs = W.make_shards(wl, 0, "bf16", 72, DEV)
+    vo = run_relayout(plan, 0, vs, "bf16").views
+    check_full(0, wl.b, wl.d, wl.seq_splits, wl.head_splits, vs, vo, threads=NT)
 
 
 # ---------------------------------------------------------------------------
@@ -706,8 +768,8 @@ def gather_device(outs, coords):
 
 def test_shards_beyond_4_gib():
     """Shards of 4.5-4.9 GB: byte offsets past 2^32 inside one shard, for both
-    modes of the relayout and for the fused band kernel (d = 128), whose lane
-    offsets are 32-bit on 64-bit block bases.  Sampled elements and rows,
+    modes of the relayout and for the fused scatter (d = 128).  Sampled
+    elements and rows,
     including the last rows of every shard, against the oracle."""
     seq, head, d = [2_200_000, 2_300_000], [4, 4], 256
     H.say(f"case: relayout uint8 W=2 seq={seq} head={head} d={d} (shards > 4 GiB)")

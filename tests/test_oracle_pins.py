@@ -217,6 +217,30 @@ def test_roundtrip_and_moved_once(seed):
         assert np.array_equal(x, z)
 
 
+@pytest.mark.parametrize("threads", [2, 5, 8])
+def test_threaded_loops_equal_single_thread(threads):
+    """The threaded entry points hand destination rows to threads and must
+    give the single-threaded result exactly, for the relayout and the fused
+    row operation."""
+    rng = np.random.default_rng(500 + threads)
+    for _ in range(4):
+        world, b, d, seq, head = random_geometry(rng)
+        for mode in (0, 1):
+            xs = rand_shards(rng, mode, b, d, seq, head, np.uint16)
+            one = oracle.a2a_4d(mode, b, d, seq, head, xs)
+            many = oracle.a2a_4d(mode, b, d, seq, head, xs, threads=threads)
+            for a, c in zip(one, many):
+                assert np.array_equal(a, c)
+    b, d, seq, head = 2, 64, [40, 3, 21], [2, 1, 3]
+    xs = [torch_bf16_bits(rng.standard_normal((b, S, 6, d))) for S in seq]
+    gamma = (rng.random(d) + 0.5).astype(np.float32)
+    c, s = oracle.rope_table(10000.0, 64, d)
+    one = oracle.qknorm_rope_mode0(b, d, seq, head, xs, gamma, 1e-6, c, s)
+    many = oracle.qknorm_rope_mode0(b, d, seq, head, xs, gamma, 1e-6, c, s, threads=threads)
+    for a, m in zip(one, many):
+        assert np.array_equal(a, m)
+
+
 def test_world_one_is_identity():
     rng = np.random.default_rng(7)
     for mode in (0, 1):
