@@ -187,6 +187,29 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
                            void *const *dst, void *const *window, hipStream_t stream);
 
 /*
+ * ulysses_a2a_4d_chunked with the library's own windows, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the W windows live in one static
+ * device array of ULYSSES_STATIC_WINDOW_BYTES (64 MiB) that every GPU running
+ * the library holds until the process ends.  The call itself allocates and
+ * frees nothing.  Window r starts at r times the per-rank window bytes
+ * rounded up to 256.
+ *
+ * The result equals ulysses_a2a_4d_chunked with caller windows.  The array
+ * is shared by every call on a GPU and keeps the last call's contents (the
+ * windows need no clearing: each plane's relayout writes every window byte
+ * the copy-out reads), so calls that overlap in time on one GPU, e.g. on two
+ * streams, race; serialise them.
+ *
+ * EINVAL when the plan has no cap; EWINDOW when the per-rank window bytes
+ * exceed the cap, or when W windows do not fit the array; EHIP when the
+ * array's address cannot be found on the stream's device.
+ */
+#define ULYSSES_STATIC_WINDOW_BYTES (64ll << 20)
+int ulysses_a2a_4d_chunked_static(const ulysses_plan *plan, int mode, const void *const *src,
+                                  void *const *dst, hipStream_t stream);
+
+/*
  * Mode-0 relayout of q and k with QK RMSNorm and RoPE applied while
  * scattering (0.1.0 "What it does": the QK RMSNorm + RoPE fusion inside the
  * scatter kernel; the pages give no formula, so the operation is fixed here).

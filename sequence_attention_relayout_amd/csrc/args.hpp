@@ -22,6 +22,12 @@ constexpr uint32_t kNone = 0xFFFFFFFFu;
 // four for the fused scatter.
 constexpr uint32_t kRelayoutBlock = 64;
 constexpr uint32_t kFusedBlock = 256;
+// Bytes of the static device array that holds the windows of the
+// plane-at-a-time call for callers that cannot allocate (one array per GPU
+// the library runs on, kept until the process ends), and the alignment of
+// each window within it.
+constexpr uint64_t kStaticWindowBytes = uint64_t{64} << 20;
+constexpr uint64_t kStaticWindowAlign = 256;
 
 // floor(n / d) for every 32-bit n, from the multiplier and shifts that
 // div32_magic gives for d (Granlund & Montgomery, "Division by invariant

@@ -317,6 +317,43 @@ int ulysses_a2a_4d_chunked(const ulysses_plan *plan, int mode, const void *const
     });
 }
 
+int ulysses_a2a_4d_chunked_static(const ulysses_plan *plan, int mode, const void *const *src,
+                                  void *const *dst, hipStream_t stream) {
+    return guarded([&]() -> int {
+        int rc = check_plan_mode(plan, mode);
+        if (rc) return rc;
+        const ulysses::Plan &p = plan->p;
+        if (p.window_cap <= 0)
+            return set_error(ULYSSES_EINVAL, "the plan has no window cap (window_cap_bytes = 0)");
+        const int64_t wb = p.mode[mode].window_bytes;
+        if (wb > p.window_cap)
+            return set_error(ULYSSES_EWINDOW, "window bytes per rank per plane " +
+                                                  std::to_string(wb) + " exceed the cap " +
+                                                  std::to_string(p.window_cap));
+        // the W windows, each rounded up to the array's alignment, must fit
+        const uint64_t align = ulysses::kStaticWindowAlign;
+        const uint64_t slot = (static_cast<uint64_t>(wb) + align - 1) / align * align;
+        if (slot * static_cast<uint64_t>(p.world) > ulysses::kStaticWindowBytes)
+            return set_error(ULYSSES_EWINDOW,
+                             std::to_string(p.world) + " windows of " + std::to_string(wb) +
+                                 " bytes exceed the static window array of " +
+                                 std::to_string(ulysses::kStaticWindowBytes) + " bytes");
+        std::vector<Range> ranges;
+        rc = check_shards(p, mode, src, dst, "src", "dst", &ranges);
+        if (rc) return rc;
+        unsigned char *base = nullptr;
+        rc = launch_status(ulysses::static_windows(stream, &base), "static windows");
+        if (rc) return rc;
+        add_range(&ranges, base, static_cast<int64_t>(ulysses::kStaticWindowBytes), true,
+                  "the static windows");
+        rc = check_overlap(ranges);
+        if (rc) return rc;
+        const void *window[ulysses::kMaxWorld];
+        for (int r = 0; r < p.world; ++r) window[r] = base + slot * static_cast<uint64_t>(r);
+        return chunked_planes(p, mode, src, dst, window, stream);
+    });
+}
+
 int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_src,
                                void *const *q_dst, const void *const *k_src,
                                void *const *k_dst, const float *gamma_q, const float *gamma_k,

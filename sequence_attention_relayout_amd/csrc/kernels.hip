@@ -25,6 +25,8 @@
 // notes for the tables).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.hpp"
 
 namespace ulysses {
@@ -143,6 +145,43 @@ __global__ void __launch_bounds__(kRelayoutBlock) plane_copy_kernel(const CopyAr
     const uint32_t v = (x - a.blk_begin[r]) * kRelayoutBlock + threadIdx.x;
     if (v < a.nvec[r])
         store16(addr_of(a.dst[r]) + (uint64_t(v) << 4), load16(addr_of(a.src[r]) + (uint64_t(v) << 4)));
+}
+
+// The windows of the plane-at-a-time call for callers that cannot allocate.
+// In host code `scratch` only stands in for the symbol: its device address
+// on a GPU comes from hipGetSymbolAddress with that GPU current, once per
+// device, and only that address is ever handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kStaticWindowBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_windows(hipStream_t stream, unsigned char **ptr) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t back = hipSetDevice(cur);
+            if (e == hipSuccess) e = back;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch[dev] = p;
+    }
+    *ptr = static_cast<unsigned char *>(g_scratch[dev]);
+    return hipSuccess;
 }
 
 hipError_t launch_plane_copy(const CopyArgs &a, uint32_t grid_x, hipStream_t stream) {

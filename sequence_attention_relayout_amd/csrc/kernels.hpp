@@ -21,6 +21,12 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
 // threads.
 hipError_t launch_plane_copy(const CopyArgs &a, uint32_t grid_x, hipStream_t stream);
 
+// Device address of the static window array (kStaticWindowBytes) on the
+// device of `stream` (the current device for the null stream), looked up
+// once per device and kept.  The library allocates nothing here: the array
+// is part of the library's code object on each GPU.
+hipError_t static_windows(hipStream_t stream, unsigned char **ptr);
+
 // Fused QK RMSNorm + RoPE mode-0 pass over q and k for head dimension d
 // (d / 8 a power of two from 1 to 64): grid (grid_x, planes, 1) of
 // kFusedBlock threads.

@@ -60,6 +60,8 @@ def _load():
     lib.ulysses_a2a_4d_multi.restype = ctypes.c_int
     lib.ulysses_a2a_4d_chunked.argtypes = [_p, ctypes.c_int, _p, _p, _p, _p]
     lib.ulysses_a2a_4d_chunked.restype = ctypes.c_int
+    lib.ulysses_a2a_4d_chunked_static.argtypes = [_p, ctypes.c_int, _p, _p, _p]
+    lib.ulysses_a2a_4d_chunked_static.restype = ctypes.c_int
     lib.ulysses_a2a_4d_qknorm_rope.argtypes = [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                                _p, _p, _p]
     lib.ulysses_a2a_4d_qknorm_rope.restype = ctypes.c_int
@@ -256,6 +258,15 @@ def ulysses_a2a_4d_chunked(plan, mode, src, dst, window=None, stream=None):
     _check(_load().ulysses_a2a_4d_chunked(
         plan.handle, int(mode), _ptr_array(src, w, "src", plan.shard_bytes(mode, False)),
         _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)), win, _stream(stream)))
+
+
+def ulysses_a2a_4d_chunked_static(plan, mode, src, dst, stream=None):
+    """The plane-at-a-time call with the library's static windows (no
+    allocation anywhere in the call)."""
+    w = plan.world
+    _check(_load().ulysses_a2a_4d_chunked_static(
+        plan.handle, int(mode), _ptr_array(src, w, "src", plan.shard_bytes(mode, False)),
+        _ptr_array(dst, w, "dst", plan.shard_bytes(mode, True)), _stream(stream)))
 
 
 def ulysses_a2a_4d_qknorm_rope(plan, q_src, q_dst, k_src, k_dst, gamma_q, gamma_k, eps,
