@@ -94,19 +94,23 @@ def traffic_from_profile():
     return c.get("traffic_bytes_per_launch")
 
 
-def timed(fn, reps, stream, torch, warmup=3):
-    """Median and min milliseconds of fn() over reps (after `warmup` untimed
-    calls), HIP events on `stream`."""
+def timed(fn, reps, stream, torch, warmup=3, inner=10):
+    """Median and min milliseconds per call of fn(), timed like the step:
+    `inner` calls back to back between one pair of HIP events on `stream`,
+    `reps` such pairs after `warmup` untimed calls.  (An event pair around
+    every single call measured some launches up to 10% slower: the
+    per-call events, not the kernels, set those figures.)"""
     for _ in range(warmup):
         fn()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(reps)]
-    for a, b in evs:
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(reps)]
+    for a, b in pairs:
         a.record(stream)
-        fn()
+        for _ in range(inner):
+            fn()
         b.record(stream)
     torch.cuda.synchronize()
-    ts = [a.elapsed_time(b) for a, b in evs]
+    ts = [a.elapsed_time(b) / inner for a, b in pairs]
     return statistics.median(ts), min(ts)
 
 
@@ -188,9 +192,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time the step only")
+    ap.add_argument("--rows", default=",".join(ROW_GROUPS),
+                    help="comma-separated row groups to time after the step "
+                         f"(of {', '.join(ROW_GROUPS)}); each runs only its own launches")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the HBM read/write/copy ceiling probe")
     args = ap.parse_args()
+    groups = [g for g in args.rows.split(",") if g]
+    bad = [g for g in groups if g not in ROW_GROUPS]
+    if bad:
+        print(f"unknown row groups {bad}; known: {list(ROW_GROUPS)}", file=sys.stderr)
+        sys.exit(2)
     world_env = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world_env != 1:
         print("bench.py measures one GPU: the W ranks are emulated as shard buffers in one "
@@ -312,7 +324,7 @@ def main():
     # ceiling ("of the fabric" in the pages' terms)
     flat_src = torch.empty(bytes0 // 2, dtype=torch.uint8, device=dev)
     flat_dst = torch.empty_like(flat_src)
-    d2d_ms, _ = timed(lambda: flat_dst.copy_(flat_src), 10, stream, torch)
+    d2d_ms, _ = timed(lambda: flat_dst.copy_(flat_src), 5, stream, torch)
     d2d = bytes0 / (d2d_ms * 1e-3) / 1e9
     del flat_src, flat_dst
 
@@ -358,20 +370,36 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_rows:
-        result["rows"] = time_rows(U, W, torch, dev, stream)
+        result["rows"] = time_rows(U, W, torch, dev, stream, groups)
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on a bounded sample ...")
         result["cpu_baseline"] = cpu_baseline()
     print(json.dumps(result), flush=True)
 
 
-def time_rows(U, W, torch, dev, stream, reps=20):
+ROW_GROUPS = ("uneven", "tiny", "qkv", "chunked", "fused")
+
+
+def time_rows(U, W, torch, dev, stream, groups=ROW_GROUPS, reps=7):
     """The other hot-path rows, each timed on its own (median of reps)."""
     rows = {}
-    h = stream.cuda_stream
-    wls = W.workloads()
+    if "uneven" in groups:
+        rows.update(rows_uneven(U, W, torch, dev, stream, reps))
+    if "tiny" in groups:
+        rows.update(rows_tiny(U, W, torch, dev, stream))
+    if "qkv" in groups:
+        rows.update(rows_qkv(U, W, torch, dev, stream, reps))
+    if "chunked" in groups:
+        rows.update(rows_chunked(U, W, torch, dev, stream))
+    if "fused" in groups:
+        rows.update(rows_fused(U, W, torch, dev, stream, reps))
+    return rows
 
-    wl = wls["w7_uneven"]
+
+def rows_uneven(U, W, torch, dev, stream, reps):
+    rows = {}
+    h = stream.cuda_stream
+    wl = W.workloads()["w7_uneven"]
     for dt in wl.dtypes:
         plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, dt)
         for mode in (0, 1):
@@ -403,9 +431,14 @@ def time_rows(U, W, torch, dev, stream, reps=20):
         del xs, ys
     torch.cuda.empty_cache()
     log("uneven rows done")
+    return rows
 
+
+def rows_tiny(U, W, torch, dev, stream):
     # the two-rank example: launch-bound, so this is latency, not bandwidth
-    wl = wls["w2_tiny"]
+    rows = {}
+    h = stream.cuda_stream
+    wl = W.workloads()["w2_tiny"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
     xs = W.make_shards(wl, 0, "bf16", wl.seed, dev)
     ys = [torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16, device=dev)
@@ -416,7 +449,7 @@ def time_rows(U, W, torch, dev, stream, reps=20):
         U.ulysses_a2a_4d(plan, 0, xs, ys, h)
         U.ulysses_a2a_4d(plan, 1, ys, zs, h)
 
-    med_tiny, _ = timed(tiny_step, 50, stream, torch)
+    med_tiny, _ = timed(tiny_step, 10, stream, torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(500):
@@ -428,9 +461,14 @@ def time_rows(U, W, torch, dev, stream, reps=20):
                                "note": "mode 0 + mode 1 of the two-rank example (65,536 B "
                                        "per mode); host time per ABI call through Python"}
     del xs, ys, zs
+    return rows
 
+
+def rows_qkv(U, W, torch, dev, stream, reps):
     # q, k and v of the timed geometry: one launch against three
-    wl = wls["w8_wan720p"]
+    rows = {}
+    h = stream.cuda_stream
+    wl = W.workloads()["w8_wan720p"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
     xs = [W.make_shards(wl, 0, "bf16", 130 + t, dev) for t in range(3)]
     ys = [[torch.empty(U.ulysses_plan_shape(plan, 0, r, True), dtype=torch.bfloat16,
@@ -465,10 +503,15 @@ def time_rows(U, W, torch, dev, stream, reps=20):
     del xs, ys, xg, gy
     torch.cuda.empty_cache()
     log("multi-tensor rows done")
+    return rows
 
+
+def rows_chunked(U, W, torch, dev, stream):
     # the FastVideo pack, plane at a time: through the windows (relayout,
     # then copy-out), straight into the destination planes, and in one pass
-    wl = wls["w4_qkv_chunked"]
+    rows = {}
+    h = stream.cuda_stream
+    wl = W.workloads()["w4_qkv_chunked"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16",
                                  wl.window_cap_bytes)
     xs = W.make_shards(wl, 0, "bf16", wl.seed, dev)
@@ -477,11 +520,11 @@ def time_rows(U, W, torch, dev, stream, reps=20):
     win = [torch.empty(U.ulysses_plan_window_bytes(plan, 0), dtype=torch.uint8, device=dev)
            for _ in range(wl.world)]
     relayout_bytes = U.ulysses_plan_bytes(plan, 0)
-    staged, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win, h), 5, stream,
-                      torch)
-    direct, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, None, h), 5, stream,
-                      torch)
-    one_pass, _ = timed(lambda: U.ulysses_a2a_4d(plan, 0, xs, ys, h), 5, stream, torch)
+    staged, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, win, h), 3, stream,
+                      torch, inner=3)
+    direct, _ = timed(lambda: U.ulysses_a2a_4d_chunked(plan, 0, xs, ys, None, h), 3, stream,
+                      torch, inner=3)
+    one_pass, _ = timed(lambda: U.ulysses_a2a_4d(plan, 0, xs, ys, h), 3, stream, torch, inner=3)
     rows["w4_qkv_chunked_mode0"] = {
         "staged_gbs_relayout_bytes": round(relayout_bytes / (staged * 1e-3) / 1e9, 1),
         "staged_gbs_moved_bytes": round(2 * relayout_bytes / (staged * 1e-3) / 1e9, 1),
@@ -498,8 +541,13 @@ def time_rows(U, W, torch, dev, stream, reps=20):
     del xs, ys, win
     torch.cuda.empty_cache()
     log("chunked rows done")
+    return rows
 
-    wl = wls["w8_fused_qknorm_rope"]
+
+def rows_fused(U, W, torch, dev, stream, reps):
+    rows = {}
+    h = stream.cuda_stream
+    wl = W.workloads()["w8_fused_qknorm_rope"]
     plan = U.ulysses_plan_create(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, "bf16")
     q = W.make_shards(wl, 0, "bf16", 70, dev)
     k = W.make_shards(wl, 0, "bf16", 71, dev)

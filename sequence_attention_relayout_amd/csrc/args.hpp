@@ -19,7 +19,7 @@ constexpr uint32_t kMaxRowVectors = 32768;
 // Threshold entries past the world; no key reaches them.
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 // Threads per block: one wave per block for the relayout and the plane copy,
-// four for the fused scatter.
+// four for the fused pass.
 constexpr uint32_t kRelayoutBlock = 64;
 constexpr uint32_t kFusedBlock = 256;
 // Bytes of the static device array that holds the windows of the
@@ -106,30 +106,27 @@ struct CopyArgs {
     uint32_t nvec[kMaxWorld];
 };
 
-// The fused QK-norm + RoPE mode-0 pass, walking every source vector once (a
-// scatter): grid.x takes the source shards one after another, kFusedBlock
-// consecutive vectors of a shard per block; grid.y the batch planes (the
-// caller points src and dst at the launch's first plane).  Both q and k move
-// in every block, so the rotary rows a block reads serve both.
+// The fused QK-norm + RoPE mode-0 pass, walking every destination vector
+// once (a gather, like RelayoutArgs in mode 0): grid.x takes the destination
+// shards one after another, kFusedBlock consecutive vectors of a shard per
+// block; grid.y the batch planes (the caller points src and dst at the
+// launch's first plane).  Each lane moves the same vector of q and of k.
 //
-// Source shard j's rows are the full rows of G / 16 = n_global * d / 8
-// vectors (the same split for every j); column col belongs to the
-// destination rank r = the number of q in [1, world) with bound[q] <= col,
-// and lands at off[j][r] + row * pitch[j][r] + col of destination plane r.
-// Source row `row` of shard j sits at global sequence position pos0[j] +
-// row.
+// Destination shard r's rows are sequence positions s, of
+// row[r].vpr = H_r * d / 8 vectors.  Row s comes from source rank j = the
+// number of q in [1, world) with bound[q] <= s, vector (s, col) at
+// off[r][j] + s * pitch + col of source plane j, and takes rotary row s.
 struct FusedArgs {
     const unsigned char *src[2][kMaxWorld];   // [0] q, [1] k
     unsigned char *dst[2][kMaxWorld];
-    uint64_t src_plane[kMaxWorld];
-    uint64_t dst_plane[kMaxWorld];
-    int64_t off[kMaxWorld][kMaxWorld];        // [j][r]
-    uint32_t pitch[kMaxWorld][kMaxWorld];     // [j][r]
-    uint32_t blk_begin[kMaxWorld];            // first block of source j; kNone past the world
-    uint32_t nvec[kMaxWorld];                 // vectors per plane of source j
-    uint32_t pos0[kMaxWorld];
-    uint32_t bound[kMaxWorld];
-    RowSplit row;                             // rows of every source shard
+    uint64_t src_plane[kMaxWorld];            // vectors per batch plane of source shard j
+    uint64_t dst_plane[kMaxWorld];            // vectors per batch plane of destination shard r
+    int64_t off[kMaxWorld][kMaxWorld];        // [r][j]
+    uint32_t pitch;                           // vectors per source row (every j)
+    uint32_t blk_begin[kMaxWorld];            // first block of destination r; kNone past the world
+    uint32_t nvec[kMaxWorld];                 // vectors per plane of destination r
+    RowSplit row[kMaxWorld];                  // rows of destination r
+    uint32_t bound[kMaxWorld];                // [0] unused; kNone past the world
     const float *gamma[2];
     const float *rope_cos;
     const float *rope_sin;

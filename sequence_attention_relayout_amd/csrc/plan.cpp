@@ -232,27 +232,24 @@ uint64_t fill_fused(const Plan &p, FusedArgs *a) {
         a->blk_begin[q] = kNone;
         a->bound[q] = kNone;
     }
-    // Pieces sharing source j partition its columns by destination head
-    // block (the same bounds for every j).
-    for (int r = 1; r < w; ++r) a->bound[r] = static_cast<uint32_t>(g.piece[r].src_col0 / 16);
-    a->row = row_split(static_cast<uint32_t>(p.G / 16));
+    // the source sequence ranges partition every destination's rows
+    for (int j = 1; j < w; ++j) a->bound[j] = static_cast<uint32_t>(g.piece[j * w].dst_row0);
+    a->pitch = static_cast<uint32_t>(p.G / 16);
     a->half_d = static_cast<uint32_t>(p.d / 2);
     a->inv_d = 1.0f / static_cast<float>(p.d);   // exact for the power-of-two d accepted
     uint64_t blocks = 0;
-    for (int j = 0; j < w; ++j) {
-        a->src_plane[j] = static_cast<uint64_t>(g.src_plane[j] / 16);
-        a->dst_plane[j] = static_cast<uint64_t>(g.dst_plane[j] / 16);
-        a->nvec[j] = static_cast<uint32_t>(g.src_plane[j] / 16);
-        a->pos0[j] = static_cast<uint32_t>(p.seq_off[j]);
-        a->blk_begin[j] = static_cast<uint32_t>(blocks);
-        blocks += (uint64_t(a->nvec[j]) + kFusedBlock - 1) / kFusedBlock;
-        for (int r = 0; r < w; ++r) {
-            // source (row, col) of piece j -> r lands at destination vector
-            // dst_off + (row - src_row0) * dst_pitch + (col - src_col0)
+    for (int r = 0; r < w; ++r) {
+        a->src_plane[r] = static_cast<uint64_t>(g.src_plane[r] / 16);
+        a->dst_plane[r] = static_cast<uint64_t>(g.dst_plane[r] / 16);
+        a->row[r] = row_split(static_cast<uint32_t>(p.R[r] / 16));
+        a->nvec[r] = static_cast<uint32_t>(g.dst_plane[r] / 16);
+        a->blk_begin[r] = static_cast<uint32_t>(blocks);
+        blocks += (uint64_t(a->nvec[r]) + kFusedBlock - 1) / kFusedBlock;
+        for (int j = 0; j < w; ++j) {
+            // destination (row, col) of piece j -> r reads source vector
+            // src_off + (row - dst_row0) * src_pitch + (col - dst_col0)
             const Piece &pc = g.piece[j * w + r];
-            a->off[j][r] =
-                (pc.dst_off - pc.src_row0 * pc.dst_pitch - pc.src_col0) / 16;
-            a->pitch[j][r] = static_cast<uint32_t>(pc.dst_pitch / 16);
+            a->off[r][j] = (pc.src_off - pc.dst_row0 * pc.src_pitch - pc.dst_col0) / 16;
         }
     }
     return blocks;

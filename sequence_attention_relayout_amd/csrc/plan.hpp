@@ -83,7 +83,7 @@ uint64_t fill_relayout(const Plan &p, int mode, RelayoutArgs *a);
 // into the destination shards of `mode` (CopyArgs).  Returns grid.x.
 uint64_t fill_plane_copy(const Plan &p, int mode, CopyArgs *a);
 
-// Launch table of the fused mode-0 scatter (FusedArgs) with kFusedBlock
+// Launch table of the fused mode-0 gather (FusedArgs) with kFusedBlock
 // vectors per block; pointers, gains, tables and eps are left to the caller.
 // Returns grid.x.
 uint64_t fill_fused(const Plan &p, FusedArgs *a);

@@ -11,9 +11,9 @@
 //     clamp included);
 //   - the plane copy of the plane-at-a-time mode covers each destination
 //     plane once from the same offset in the window;
-//   - the fused scatter's lane within its head row is the thread's lane
+//   - the fused gather's lane within its head row is the thread's lane
 //     modulo d/8, valid lanes come in whole head rows, and the rotary row is
-//     the global position of the source row;
+//     the global position of the destination row;
 //   - the divisions are exact (the multiply-high by the row length at every
 //     quotient boundary, hence everywhere, both sides being monotone; the
 //     32-bit division of div32 against '/').
@@ -167,36 +167,42 @@ static void check_plane_copy(const Plan &p, int mode) {
         for (size_t i = 0; i < hits[r].size(); ++i) REQUIRE(hits[r][i] == 1, "copy coverage");
 }
 
-// The fused scatter (mode 0, bf16, L = d/8 lanes per head row).
+// The fused gather (mode 0, bf16, L = d/8 lanes per head row).
 static void check_fused(const Plan &p) {
     FusedArgs a;
     const uint64_t gx = fill_fused(p, &a);
     const uint32_t L = static_cast<uint32_t>(p.d / 8);
     const ModeGeom &g = p.mode[0];
     REQUIRE(a.half_d == uint32_t(p.d / 2) && a.inv_d * float(p.d) == 1.0f, "fused constants");
+    REQUIRE(a.pitch == uint32_t(p.G / 16), "fused source pitch");
+    // the kernel takes the last q with bound[q] <= row, which is the count
+    // of such q only for ascending bounds
+    for (int q = 2; q < kMaxWorld; ++q) REQUIRE(a.bound[q] >= a.bound[q - 1], "fused bounds ascend");
     std::vector<std::vector<int>> hits(p.world);
     for (int r = 0; r < p.world; ++r) hits[r].assign(static_cast<size_t>(p.b * g.dst_plane[r] / 16), 0);
     for (uint32_t y = 0; y < p.b; ++y)
         for (uint32_t x = 0; x < gx; ++x) {
-            const uint32_t j = find_group(a.blk_begin, x);
-            REQUIRE(j < uint32_t(p.world), "fused block past the world");
-            const uint32_t s0 = (x - a.blk_begin[j]) * kFusedBlock;
-            REQUIRE(s0 < a.nvec[j], "fused block starts past its shard");
-            const uint32_t last = a.nvec[j] - 1;
+            const uint32_t r = find_group(a.blk_begin, x);
+            REQUIRE(r < uint32_t(p.world), "fused block past the world");
+            const uint32_t s0 = (x - a.blk_begin[r]) * kFusedBlock;
+            REQUIRE(s0 < a.nvec[r], "fused block starts past its shard");
+            const uint32_t last = a.nvec[r] - 1;
+            REQUIRE(int64_t(a.row[r].vpr) == p.H[r] * L, "fused destination row length");
             for (uint32_t tid = 0; tid < kFusedBlock; ++tid) {
                 const bool ok = s0 + tid <= last;
                 const uint32_t lt = std::min(s0 + tid, last) - s0;
                 const uint32_t lane = tid & (L - 1);
                 uint32_t row, col;
-                split_rows(a.row, s0, lt, &row, &col);
-                const uint32_t r = find_group(a.bound, col);
-                REQUIRE(r < uint32_t(p.world), "fused owner past the world");
+                split_rows(a.row[r], s0, lt, &row, &col);
+                const uint32_t j = find_group(a.bound, row);
+                REQUIRE(j < uint32_t(p.world), "fused source past the world");
                 // the loads of every lane (clamped ones too) stay in bounds
                 // (one launch holds every plane here: b <= 65535)
-                const uint64_t sv = uint64_t(y) * a.src_plane[j] + s0 + lt;
-                REQUIRE(sv < uint64_t(p.b) * a.src_plane[j], "fused load past shard");
-                const uint64_t pos = uint64_t(a.pos0[j]) + row;
-                REQUIRE(pos < uint64_t(p.s_global), "rotary row past the table");
+                const int64_t sv = int64_t(uint64_t(y) * a.src_plane[j]) + a.off[r][j] +
+                                   int64_t(uint64_t(row) * a.pitch + col);
+                REQUIRE(sv >= 0 && sv < int64_t(uint64_t(p.b) * a.src_plane[j]),
+                        "fused load past shard");
+                REQUIRE(row < uint64_t(p.s_global), "rotary row past the table");
                 REQUIRE(4 * lane + 3 < a.half_d && 8 * lane + 7 < uint32_t(p.d), "lane past d");
                 if (!ok) {
                     // a clamped lane's whole head row is past the shard
@@ -204,17 +210,17 @@ static void check_fused(const Plan &p) {
                     continue;
                 }
                 REQUIRE(col % L == lane, "lane %u holds column %u of a %u-lane row", tid, col, L);
-                const int64_t dv = int64_t(uint64_t(y) * a.dst_plane[r]) + a.off[j][r] +
-                                   int64_t(uint64_t(row) * a.pitch[j][r] + col);
-                REQUIRE(dv >= 0 && dv < int64_t(hits[r].size()), "fused store past shard");
+                const uint64_t dv = uint64_t(y) * a.dst_plane[r] + s0 + lt;
+                REQUIRE(dv < hits[r].size(), "fused store past shard");
+                REQUIRE(uint64_t(row) * a.row[r].vpr + col == s0 + lt, "fused row split");
                 hits[r][dv] += 1;
                 int want_j;
                 int64_t want_src;
-                defined_source(p, 0, int(r), dv, &want_j, &want_src);
-                REQUIRE(int(j) == want_j && int64_t(sv) == want_src, "fused source");
+                defined_source(p, 0, int(r), int64_t(dv), &want_j, &want_src);
+                REQUIRE(int(j) == want_j && sv == want_src, "fused source");
                 // rotary row of the destination row's global position
-                const int64_t Sg = (dv / (p.H[r] * L)) % p.s_global;
-                REQUIRE(int64_t(pos) == Sg, "fused rotary position");
+                const int64_t Sg = (int64_t(dv) / (p.H[r] * L)) % p.s_global;
+                REQUIRE(int64_t(row) == Sg, "fused rotary position");
             }
         }
     for (int r = 0; r < p.world; ++r)
