@@ -13,12 +13,13 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   value      whole-step throughput, algorithmic bytes (every element read
              once and written once) / step time, in GB/s;
   roofline   the relayout kernel: algorithmic bytes per launch / its
-             average launch time from HIP event pairs around each launch on
-             the launch stream (a second pass of K steps, so the step
-             timing itself carries no events), against 8 TB/s; `traffic`
-             comes from the rocprofv3 counter
-             summary in profiles/ when it was taken on the current kernel
-             source, else null;
+             average launch time, the timed region's event time over its 2K
+             launches (every launch of the region is that kernel), against
+             8 TB/s; per-mode medians come from a pass of at least 100
+             steps with an event pair around each launch, run before the
+             warm-up so the timed region carries no events; `traffic` comes from the
+             rocprofv3 counter summary in profiles/ when it was taken on the
+             current kernel source, else null;
   value_mall_cold  the same step with the 256 MB Infinity Cache written
              over between launches (per-mode medians), beside `value`;
   cpu_baseline  the CPU oracle on the step's geometry: its loops on all
@@ -26,7 +27,7 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   rows       the other hot-path rows timed after the step: uneven W=7 in
              four dtypes, unequal head widths, q/k/v in one launch, the
              plane-at-a-time QKV pack through windows and straight into the
-             destination, the fused QK-norm + RoPE scatter; plus a same-run
+             destination, the fused QK-norm + RoPE pass; plus a same-run
              device-to-device copy (torch) and this GPU's read / write / copy
              ceilings for 16-byte vectors (hbm_probe, run as a child process
              first).
@@ -249,29 +250,19 @@ def main():
     def mode1():
         U.ulysses_a2a_4d(plan, 1, y1, x1, h)
 
-    for _ in range(args.warmup):
-        mode0()
-        mode1()
-    torch.cuda.synchronize()
-
-    # The timed region: K steps back to back, events only at its two ends.
     K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(K):
+    # Per-launch durations of the relayout kernel: at least 100 steps with
+    # each launch between its own pair of events on the launch stream, after
+    # three untimed steps of their own (the first launches of a process load
+    # code, and the clocks take tens of milliseconds to come up; the medians
+    # absorb that).  They run before the timed region, which carries no events
+    # of its own.
+    for _ in range(3):
         mode0()
         mode1()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = start.elapsed_time(end) / K
-
-    # Per-launch durations of the relayout kernel: the same K steps again,
-    # each launch between its own pair of events on the launch stream.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    for k in range(K):
+    KE = max(K, 100)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(KE)]
+    for k in range(KE):
         evs[k][0].record(stream)
         mode0()
         evs[k][1].record(stream)
@@ -280,12 +271,6 @@ def main():
     torch.cuda.synchronize()
     m0 = [e[0].elapsed_time(e[1]) for e in evs]
     m1 = [e[1].elapsed_time(e[2]) for e in evs]
-    # Every launch of the timed region is the relayout kernel (mode 0 and
-    # mode 1 move the same bytes), so its average launch duration is the
-    # region's event time over its 2K launches; the per-launch event pairs
-    # above give the per-mode medians (they add the events' own overhead).
-    launch_ms = ms_step / 2
-    launch_ms_event_pairs = statistics.mean(m0 + m1)
 
     # The same launches with the 256 MB Infinity Cache (MALL) cold: 1 GiB is
     # written between launches, outside the events.
@@ -304,6 +289,30 @@ def main():
     c0 = [e[0].elapsed_time(e[1]) for e in cold]
     c1 = [e[2].elapsed_time(e[3]) for e in cold]
     del flush
+
+    for _ in range(args.warmup):
+        mode0()
+        mode1()
+    torch.cuda.synchronize()
+
+    # The timed region: K steps back to back, events only at its two ends.
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(K):
+        mode0()
+        mode1()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = start.elapsed_time(end) / K
+    # Every launch of the timed region is the relayout kernel (mode 0 and
+    # mode 1 move the same bytes), so its average launch duration is the
+    # region's event time over its 2K launches; the per-launch event pairs
+    # above give the per-mode medians (they add the events' own overhead).
+    launch_ms = ms_step / 2
+    launch_ms_event_pairs = statistics.median(m0 + m1)
 
     # A second timed region like the first, for the spread between two
     # invocations of the same K steps.
@@ -345,7 +354,8 @@ def main():
                      "traffic": traffic_from_profile(),
                      "bytes_per_launch": bytes0, "avg_launch_us": round(launch_ms * 1e3, 2),
                      "launches_timed": 2 * K,
-                     "avg_launch_us_event_pairs": round(launch_ms_event_pairs * 1e3, 2),
+                     "median_launch_us_event_pairs": round(launch_ms_event_pairs * 1e3, 2),
+                     "launches_event_pairs": 2 * KE,
                      "mode0_median_us": round(statistics.median(m0) * 1e3, 2),
                      "mode1_median_us": round(statistics.median(m1) * 1e3, 2),
                      "mode0_min_us": round(min(m0) * 1e3, 2),

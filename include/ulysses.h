@@ -210,9 +210,9 @@ int ulysses_a2a_4d_chunked_static(const ulysses_plan *plan, int mode, const void
                                   void *const *dst, hipStream_t stream);
 
 /*
- * Mode-0 relayout of q and k with QK RMSNorm and RoPE applied while
- * scattering (0.1.0 "What it does": the QK RMSNorm + RoPE fusion inside the
- * scatter kernel; the pages give no formula, so the operation is fixed here).
+ * Mode-0 relayout of q and k with QK RMSNorm and RoPE applied on the way
+ * (0.1.0 "What it does": the QK RMSNorm + RoPE fusion inside the scatter
+ * kernel; the pages give no formula, so the operation is fixed here).
  * For each destination row of d elements at GLOBAL sequence position S:
  *   ss  = sum of squares, fp32: one fused multiply-add chain per group of 8
  *         consecutive elements (ascending), then a pairwise tree over the d/8

@@ -260,7 +260,7 @@ int oracle_a2a_4d_sample(int mode, int world, int64_t b, int64_t d, int64_t esz,
 }
 
 /* ------------------------------------------------------------------ */
-/* Fused QK RMSNorm + RoPE on the mode-0 scatter                        */
+/* Fused QK RMSNorm + RoPE on the mode-0 relayout                       */
 /* ------------------------------------------------------------------ */
 
 /* bfloat16 <-> float.  bf16 is the top half of an IEEE binary32; rounding

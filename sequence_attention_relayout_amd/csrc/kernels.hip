@@ -10,19 +10,14 @@
 // 0.1.0 introduction: the sequence/head relayout is expressed as copy
 // strides instead of separate permute kernels).
 //
-// Both passes walk one side of the exchange in address order, 64 consecutive
+// Both passes walk the destination shards in address order, 64 consecutive
 // 16-byte vectors per wave (each load or store instruction of a wave covers
-// 1 KiB), and find for each lane the rank on the other side:
-//   - the relayout walks the destinations (a gather): every store of a wave
-//     is one contiguous KiB, and each lane reads from the piece that owns its
-//     destination row (mode 0) or column (mode 1);
-//   - the fused scatter walks the sources, so the rotary row of a sequence
-//     position is read by the waves of that position at the same time, and
-//     each lane writes to the rank that owns its head.
-// Measured on MI355X: walking the destination beats walking the source and
-// the earlier per-piece band walk for the relayout in both modes; for the
-// fused pass the source walk with four-wave blocks wins (see the design
-// notes for the tables).
+// 1 KiB), and find for each lane the source rank that owns its vector (a
+// gather): every store of a wave is one contiguous KiB, and each lane reads
+// from the piece that owns its destination row (mode 0, and the fused pass)
+// or column (mode 1).  Measured on MI355X, walking the destinations beats
+// walking the sources (a scatter) and the earlier per-piece band walk, for
+// the relayout in both modes and for the fused pass.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -84,7 +79,7 @@ __device__ __forceinline__ RowCol split_rows(const RowSplit &rs, uint32_t s0, ui
 }
 
 // --------------------------------------------------------------------------
-// Relayout (modes 0 and 1, and the scatter of the plane-at-a-time mode)
+// Relayout (modes 0 and 1, and the window pass of the plane-at-a-time mode)
 // --------------------------------------------------------------------------
 
 // Each wave moves 1 KiB, so what a wave does before its load issues bounds
@@ -207,7 +202,7 @@ hipError_t launch_plane_copy(const CopyArgs &a, uint32_t grid_x, hipStream_t str
 // way: each lane takes one destination vector of q and the same one of k,
 // reads both from the source rank that owns the row's sequence position, and
 // stores them normalised and rotated, so every store of a wave is one
-// contiguous KiB.  Measured on MI355X it beats walking the sources (the
+// contiguous KiB.  Measured on MI355X it beats walking the sources (a
 // scatter) by 3-6%; the data movement alone, with the arithmetic and the
 // tables taken out, runs at the same speed, so the arithmetic is hidden.
 //

@@ -236,7 +236,7 @@ static void check_geometry(int world, int64_t b, int64_t d, int dtype,
     REQUIRE(rc == kOk, "plan_build failed: %s", msg.c_str());
     for (int mode = 0; mode < 2; ++mode) {
         check_relayout(p, mode, 1 << 16, 1);
-        check_relayout(p, mode, 1 << 16, 3);      // three tensors in one launch
+        for (uint32_t t : {2u, 3u, 4u}) check_relayout(p, mode, 1 << 16, t);   // tensors in one launch
         if (b > 1) check_relayout(p, mode, 1, 1);   // one plane per launch (the chunked passes)
         check_plane_copy(p, mode);
     }

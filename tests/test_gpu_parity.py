@@ -531,7 +531,7 @@ def test_w4_qkv_chunked_full_size(golden):
 
 
 # ---------------------------------------------------------------------------
-# fused QK RMSNorm + RoPE on the mode-0 scatter
+# fused QK RMSNorm + RoPE on the mode-0 relayout
 # ---------------------------------------------------------------------------
 
 def rope_tables(s_global, d):
@@ -586,8 +586,8 @@ def test_fused_medium_full_compare(d, world, seq_total):
 @pytest.mark.parametrize("world,heads", [(2, [12, 9]), (1, [20]), (3, [17, 0, 8])])
 def test_fused_many_heads_full_compare(world, heads):
     """Many heads per rank (and a rank with none): with d = 128 a block of
-    the fused scatter spans head rows of several destination ranks, or
-    several source rows when the rows are short."""
+    the fused pass spans many head rows of one destination row, or several
+    destination rows when the rows are short."""
     seq = W.seeded_partition(7, 300, world) if world > 1 else [300]
     H.say(f"case: fused many heads W={world} seq={seq} head={heads}")
     plan = U.ulysses_plan_create(world, 2, 128, seq, heads, "bf16")
@@ -768,7 +768,7 @@ def gather_device(outs, coords):
 
 def test_shards_beyond_4_gib():
     """Shards of 4.5-4.9 GB: byte offsets past 2^32 inside one shard, for both
-    modes of the relayout and for the fused scatter (d = 128).  Sampled
+    modes of the relayout and for the fused pass (d = 128).  Sampled
     elements and rows,
     including the last rows of every shard, against the oracle."""
     seq, head, d = [2_200_000, 2_300_000], [4, 4], 256
