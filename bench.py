@@ -387,7 +387,7 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-ROW_GROUPS = ("uneven", "tiny", "qkv", "chunked", "fused")
+ROW_GROUPS = ("uneven", "heads", "tiny", "qkv", "chunked", "fused")
 
 
 def time_rows(U, W, torch, dev, stream, groups=ROW_GROUPS, reps=7):
@@ -395,6 +395,8 @@ def time_rows(U, W, torch, dev, stream, groups=ROW_GROUPS, reps=7):
     rows = {}
     if "uneven" in groups:
         rows.update(rows_uneven(U, W, torch, dev, stream, reps))
+    if "heads" in groups:
+        rows.update(rows_heads(U, W, torch, dev, stream, reps))
     if "tiny" in groups:
         rows.update(rows_tiny(U, W, torch, dev, stream))
     if "qkv" in groups:
@@ -423,8 +425,14 @@ def rows_uneven(U, W, torch, dev, stream, reps):
                 "bytes": nb}
             del xs, ys
         torch.cuda.empty_cache()
+    log("uneven rows done")
+    return rows
 
-    # unequal head widths (6 and 4 heads per rank): the row-aligned walk
+
+def rows_heads(U, W, torch, dev, stream, reps):
+    # unequal head widths (6 and 4 heads per rank)
+    rows = {}
+    h = stream.cuda_stream
     world, heads = 8, [6, 6, 6, 6, 4, 4, 4, 4]
     seq = W.even_splits(75600, world)
     plan = U.ulysses_plan_create(world, 1, 128, seq, heads, "bf16")
@@ -440,7 +448,7 @@ def rows_uneven(U, W, torch, dev, stream, reps):
             "bytes": nb}
         del xs, ys
     torch.cuda.empty_cache()
-    log("uneven rows done")
+    log("unequal-heads rows done")
     return rows
 
 

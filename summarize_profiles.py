@@ -2,16 +2,13 @@
 """Writes the summaries under profiles/ from rocprofv3 output of bench.py.
 
     python3 summarize_profiles.py OUT
+    python3 summarize_profiles.py --commands REPO OUT   (prints the runs below)
 
 OUT holds rocprofv3 output directories (--output-format csv -o run) of
 bench.py runs on one MI355X, made from /tmp with TMPDIR=/tmp:
 
-  ktrace/   rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o run
-              -- python3 bench.py --no-cpu-baseline --no-ceilings
-            (its stdout and stderr in OUT/ktrace.log)
-  <pass>/   one per entry of PASSES:
-            rocprofv3 --pmc <counters> --output-format csv -d OUT/<pass> -o run
-              -- python3 bench.py BENCH_PMC_ARGS
+  ktrace/   TRACE_CMD (its stdout and stderr in OUT/ktrace.log)
+  <pass>/   one per entry of PASSES (pmc_cmd)
 
 Every counter is averaged per (kernel, grid size) over its dispatches.  The
 summaries name the kernels by what they run (the W=8 relayout step, the
@@ -29,9 +26,13 @@ PROFILES = os.path.join(ROOT, "profiles")
 sys.path.insert(0, ROOT)
 import bench  # noqa: E402  (kernel_source_hash, PEAK_GBS)
 
-BENCH_PMC_ARGS = "--no-cpu-baseline --no-ceilings --steps 5 --warmup 1 --rows fused,chunked"
+BENCH_PMC_ARGS = ("--no-cpu-baseline --no-ceilings --steps 5 --warmup 1 "
+                  "--rows uneven,chunked,fused")
+# The unequal-heads rows launch the relayout with the same grid as the W=8
+# step, so the trace run leaves them out.
 TRACE_CMD = ("rocprofv3 --kernel-trace --stats --output-format csv -d OUT/ktrace -o run "
-             "-- python3 REPO/bench.py --no-cpu-baseline --no-ceilings")
+             "-- python3 REPO/bench.py --no-cpu-baseline --no-ceilings "
+             "--rows uneven,tiny,qkv,chunked,fused")
 # One counter pass per run: rocprofv3 does not split counters over passes.
 PASSES = {
     "fetch": ["FETCH_SIZE"],
@@ -83,6 +84,37 @@ WORKLOADS = [
 ]
 
 
+def relayout_threads(world, b, d, S, H, esz, mode):
+    """Threads of one relayout launch: 64-vector blocks per destination shard,
+    b planes along grid.y."""
+    s_global, n_global = sum(S), sum(H)
+    blocks = 0
+    for r in range(world):
+        rows, per_row = (s_global, H[r]) if mode == 0 else (S[r], n_global)
+        blocks += -(-(rows * per_row * d * esz // 16) // 64)
+    return blocks * 64 * b
+
+
+def uneven_workloads():
+    """The W=7 uneven relayout rows: one entry per byte width and mode (the
+    fp8 and int8 rows share a geometry, so they are summarised together)."""
+    from sequence_attention_relayout_amd import workloads as W
+    wl = W.workloads()["w7_uneven"]
+    out = []
+    for esz, name in ((2, "bf16"), (4, "fp32"), (1, "fp8_int8")):
+        for mode in (0, 1):
+            out.append((
+                f"w7_uneven_{name}_mode{mode}", "relayout_kernel<true>",
+                relayout_threads(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, esz, mode),
+                2 * wl.b * sum(wl.seq_splits) * sum(wl.head_splits) * wl.d * esz,
+                f"the uneven W=7 relayout, mode {mode}: b=2, s_global=75,597 as "
+                f"{', '.join(f'{x:,}' for x in wl.seq_splits)}, heads "
+                f"{', '.join(map(str, wl.head_splits))}, d=128, "
+                + ("bf16" if esz == 2 else "fp32" if esz == 4 else
+                   "1-byte elements (the fp8 e4m3 and int8 rows together)")))
+    return out
+
+
 def short(name):
     n = name.replace("void ", "").replace("ulysses::", "")
     return n[:n.index("(")] if "(" in n else n
@@ -126,7 +158,18 @@ def stats_row(name, ds):
             f"| {min(ds):.1f} | {max(ds):.1f} |")
 
 
+def commands(repo, out):
+    """The rocprofv3 runs that make OUT, one per line, each with its own time
+    limit (run them from /tmp with TMPDIR=/tmp)."""
+    cmds = ["timeout -k 10 600 " + TRACE_CMD + " > OUT/ktrace.log 2>&1"]
+    cmds += [pmc_cmd(p) + f" > OUT/{p}.log 2>&1" for p in PASSES]
+    return [c.replace("REPO", repo).replace("OUT", out) for c in cmds]
+
+
 def main():
+    if len(sys.argv) == 4 and sys.argv[1] == "--commands":
+        print("\n".join(commands(sys.argv[2], sys.argv[3])))
+        return
     if len(sys.argv) != 2:
         print(__doc__, file=sys.stderr)
         sys.exit(2)
@@ -141,7 +184,7 @@ def main():
     write_factor = CALIBRATION_BYTES / (cal["WRITE_SIZE"] * 1024) if "WRITE_SIZE" in cal else None
     cal_trace = tr.get(CALIBRATION, [])
     table = []
-    for stem, kern, grid, nbytes, what in WORKLOADS:
+    for stem, kern, grid, nbytes, what in WORKLOADS + uneven_workloads():
         ds = tr.get((kern, grid), [])
         c = cm.get((kern, grid), {})
         if not ds:
