@@ -95,14 +95,28 @@ T *plane_ptr(T *base, int64_t planes, int64_t plane_bytes) {
                                  static_cast<uintptr_t>(planes * plane_bytes));
 }
 
-// A relayout over the plan's b batch planes, at most kMaxGridY per launch,
+// Planes per launch.  A plane that moves at least kPlaneLaunchBytes (about
+// 10 us of HBM time) gets a launch of its own: the kernels' one-plane form
+// has no per-lane plane arithmetic, and measured on MI355X (W=7, b=2, 1.5-6 GB
+// per launch) it beats one launch over both planes by 1-2% despite the launch
+// boundary.  Smaller planes share launches, up to kMaxGridY each.
+constexpr int64_t kPlaneLaunchBytes = int64_t{64} << 20;
+
+int64_t planes_per_launch(const ulysses::ModeGeom &g, int world, int tensors) {
+    int64_t plane = 0;
+    for (int r = 0; r < world; ++r) plane += 2 * g.dst_plane[r];
+    return plane * tensors >= kPlaneLaunchBytes ? 1 : ulysses::kMaxGridY;
+}
+
+// A relayout over the plan's b batch planes, planes_per_launch() per launch,
 // each launch's shards pointed at its first plane.
 int launch_planes(const ulysses::Plan &p, int mode, ulysses::RelayoutArgs a, uint32_t gx,
                   int tensors, const void *const *src, void *const *dst, hipStream_t stream,
                   const char *what) {
     const ulysses::ModeGeom &g = p.mode[mode];
-    for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
-        const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
+    const int64_t per = planes_per_launch(g, p.world, tensors);
+    for (int64_t p0 = 0; p0 < p.b; p0 += per) {
+        const int64_t n = p.b - p0 < per ? p.b - p0 : per;
         for (int t = 0; t < tensors; ++t)
             for (int r = 0; r < p.world; ++r) {
                 a.src[t][r] = plane_ptr(static_cast<const unsigned char *>(src[t * p.world + r]),
@@ -398,8 +412,9 @@ int ulysses_a2a_4d_qknorm_rope(const ulysses_plan *plan, const void *const *q_sr
         a.rope_sin = rope_sin;
         a.eps = eps;
         const ulysses::ModeGeom &g = p.mode[0];
-        for (int64_t p0 = 0; p0 < p.b; p0 += ulysses::kMaxGridY) {
-            const int64_t n = p.b - p0 < ulysses::kMaxGridY ? p.b - p0 : ulysses::kMaxGridY;
+        const int64_t per = planes_per_launch(g, p.world, 2);
+        for (int64_t p0 = 0; p0 < p.b; p0 += per) {
+            const int64_t n = p.b - p0 < per ? p.b - p0 : per;
             for (int r = 0; r < p.world; ++r) {
                 a.src[0][r] =
                     plane_ptr(static_cast<const unsigned char *>(q_src[r]), p0, g.src_plane[r]);

@@ -583,6 +583,51 @@ def test_fused_medium_full_compare(d, world, seq_total):
         assert hist[2] == 0 and hist[3] == 0
 
 
+def test_relayout_large_planes_one_launch_each():
+    """Batch planes that move 64 MiB or more get one launch each (the
+    kernel's one-plane form, the shard pointers moved to each plane on the
+    host): three fp32 planes of 73.7 MB moved, W=3 uneven, both modes,
+    every element against the oracle."""
+    world, b, d = 3, 3, 128
+    seq, head = W.seeded_partition(11, 6000, world), [4, 3, 5]
+    H.say(f"case: relayout fp32 W={world} b={b} seq={seq} head={head} (one launch per plane)")
+    plan = U.ulysses_plan_create(world, b, d, seq, head, "fp32")
+    assert U.ulysses_plan_bytes(plan, 0) // b >= 64 << 20
+    wl = W.Workload("large planes", world, b, d, seq, head)
+    for mode in (0, 1):
+        xs = W.make_shards(wl, mode, "fp32", 80 + mode, DEV)
+        ys = [torch.empty(U.ulysses_plan_shape(plan, mode, r, True), dtype=torch.float32,
+                          device=DEV) for r in range(world)]
+        U.ulysses_a2a_4d(plan, mode, xs, ys)
+        torch.cuda.synchronize()
+        check_full(mode, b, d, seq, head, xs, ys, threads=NT)
+
+
+def test_fused_large_planes_one_launch_each():
+    """The fused pass with planes of q and k that move 64 MiB or more: one
+    launch per plane.  Three planes, W=3 uneven, every element of q and k
+    against the oracle."""
+    world, b, d = 3, 3, 128
+    seq, head = W.seeded_partition(12, 6000, world), [4, 3, 5]
+    H.say(f"case: fused W={world} b={b} seq={seq} head={head} (one launch per plane)")
+    plan = U.ulysses_plan_create(world, b, d, seq, head, "bf16")
+    assert 2 * U.ulysses_plan_bytes(plan, 0) // b >= 64 << 20
+    wl = W.Workload("fused large planes", world, b, d, seq, head)
+    qs = W.make_shards(wl, 0, "bf16", 82, DEV)
+    ks = W.make_shards(wl, 0, "bf16", 83, DEV)
+    gq, gk = W.make_gamma(d, 84, DEV), W.make_gamma(d, 85, DEV)
+    tab, (oc, osn) = rope_tables(sum(seq), d)
+    qo, ko = run_fused(plan, qs, ks, gq, gk, tab)
+    for src, out, g in ((qs, qo, gq), (ks, ko, gk)):
+        want = oracle.qknorm_rope_mode0(b, d, seq, head, [H.to_np(x) for x in src],
+                                        g.cpu().numpy(), EPS, oc, osn, threads=NT)
+        hist = np.zeros(4, np.int64)
+        for o, w in zip(out, want):
+            hist += ulp_hist(H.to_np(o), w)
+        H.say(f"  ulp histogram (0,1,2,>=3): {hist.tolist()}")
+        assert hist[2] == 0 and hist[3] == 0
+
+
 @pytest.mark.parametrize("world,heads", [(2, [12, 9]), (1, [20]), (3, [17, 0, 8])])
 def test_fused_many_heads_full_compare(world, heads):
     """Many heads per rank (and a rank with none): with d = 128 a block of
