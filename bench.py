@@ -20,8 +20,9 @@ Prints ONE JSON line on stdout (progress goes to stderr):
              warm-up so the timed region carries no events; `traffic` comes from the
              rocprofv3 counter summary in profiles/ when it was taken on the
              current kernel source, else null;
-  value_mall_cold  the same step with the 256 MB Infinity Cache written
-             over between launches (per-mode medians), beside `value`;
+  value_mall_cold  the same step with 1 GiB of other data read between
+             launches, so the 256 MB Infinity Cache holds none of the
+             launch's bytes (per-mode medians), beside `value`;
   cpu_baseline  the CPU oracle on the step's geometry: its loops on all
              the host cores the process may use (value), and single-threaded;
   rows       the other hot-path rows timed after the step: uneven W=7 in
@@ -272,23 +273,26 @@ def main():
     m0 = [e[0].elapsed_time(e[1]) for e in evs]
     m1 = [e[1].elapsed_time(e[2]) for e in evs]
 
-    # The same launches with the 256 MB Infinity Cache (MALL) cold: 1 GiB is
-    # written between launches, outside the events.
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    # The same launches with the 256 MB Infinity Cache (MALL) cold: 1 GiB of
+    # other data is read between launches, outside the events.  Reading (not
+    # writing) leaves only clean lines behind, so the next launch pays no
+    # write-back of the flush itself.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     cold = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
     for k in range(K):
-        flush.fill_(k & 255)
+        sink += flush.sum()
         cold[k][0].record(stream)
         mode0()
         cold[k][1].record(stream)
-        flush.fill_((k + 128) & 255)
+        sink += flush.sum()
         cold[k][2].record(stream)
         mode1()
         cold[k][3].record(stream)
     torch.cuda.synchronize()
     c0 = [e[0].elapsed_time(e[1]) for e in cold]
     c1 = [e[2].elapsed_time(e[3]) for e in cold]
-    del flush
+    del flush, sink
 
     for _ in range(args.warmup):
         mode0()
