@@ -19,9 +19,9 @@ constexpr uint32_t kMaxRowVectors = 32768;
 // Threshold entries past the world; no key reaches them.
 constexpr uint32_t kNone = 0xFFFFFFFFu;
 // Threads per block: one wave per block for the relayout and the plane copy,
-// four for the fused pass.
+// two for the fused pass.
 constexpr uint32_t kRelayoutBlock = 64;
-constexpr uint32_t kFusedBlock = 256;
+constexpr uint32_t kFusedBlock = 128;
 // Bytes of the static device array that holds the windows of the
 // plane-at-a-time call for callers that cannot allocate (one array per GPU
 // the library runs on, kept until the process ends), and the alignment of
