@@ -44,12 +44,15 @@ struct Range {
     std::string name;
 };
 
-// Pointer checks for one buffer: non-null and 16-byte aligned when non-empty.
+// Pointer checks for one buffer: non-null, 16-byte aligned and not running
+// past the top of the address space when non-empty.
 int check_ptr(const void *ptr, int64_t bytes, const std::string &name) {
     if (bytes <= 0) return ULYSSES_OK;
     if (!ptr) return set_error(ULYSSES_EINVAL, name + " is null");
-    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
-        return set_error(ULYSSES_EALIGN, name + " is not 16-byte aligned");
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+    if (lo % 16 != 0) return set_error(ULYSSES_EALIGN, name + " is not 16-byte aligned");
+    if (lo + static_cast<uintptr_t>(bytes) < lo)
+        return set_error(ULYSSES_EINVAL, name + " runs past the end of the address space");
     return ULYSSES_OK;
 }
 
@@ -161,9 +164,6 @@ int check_shards(const ulysses::Plan &p, int mode, const void *const *src, void 
 
 // Validation and launch shared by the one-tensor and multi-tensor calls.
 int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void *const *src,
-                     void *const *dst, hipStream_t stream);
-
-int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void *const *src,
                      void *const *dst, hipStream_t stream) {
     int rc = check_plan_mode(plan, mode);
     if (rc) return rc;
@@ -196,9 +196,9 @@ int relayout_tensors(const ulysses_plan *plan, int mode, int tensors, const void
 int chunked_planes(const ulysses::Plan &p, int mode, const void *const *src, void *const *dst,
                    const void *const *window, hipStream_t stream) {
     const ulysses::ModeGeom &g = p.mode[mode];
-    ulysses::RelayoutArgs scatter;
+    ulysses::RelayoutArgs to_window;
     ulysses::CopyArgs copy;
-    const uint64_t gs = ulysses::fill_relayout(p, mode, &scatter);
+    const uint64_t gs = ulysses::fill_relayout(p, mode, &to_window);
     const uint64_t gc = ulysses::fill_plane_copy(p, mode, &copy);
     int rc = check_grid(gs > gc ? gs : gc, ulysses::kRelayoutBlock, "chunked relayout");
     if (rc) return rc;
@@ -206,9 +206,9 @@ int chunked_planes(const ulysses::Plan &p, int mode, const void *const *src, voi
         for (int r = 0; r < p.world; ++r) {
             unsigned char *out = plane_ptr(static_cast<unsigned char *>(dst[r]), plane,
                                            g.dst_plane[r]);
-            scatter.src[0][r] =
+            to_window.src[0][r] =
                 plane_ptr(static_cast<const unsigned char *>(src[r]), plane, g.src_plane[r]);
-            scatter.dst[0][r] =
+            to_window.dst[0][r] =
                 window ? static_cast<unsigned char *>(const_cast<void *>(window[r])) : out;
             if (window) {
                 copy.src[r] = static_cast<const unsigned char *>(window[r]);
@@ -216,7 +216,7 @@ int chunked_planes(const ulysses::Plan &p, int mode, const void *const *src, voi
             }
         }
         rc = launch_status(
-            ulysses::launch_relayout(scatter, static_cast<uint32_t>(gs), 1, 1, stream),
+            ulysses::launch_relayout(to_window, static_cast<uint32_t>(gs), 1, 1, stream),
             "plane relayout");
         if (rc) return rc;
         if (!window) continue;

@@ -41,6 +41,8 @@ def call_errors_before_launch():
     expect(-2, U.ulysses_a2a_4d, plan, 1, src, [dst[0], dst[1] + 4], 0)
     expect(-5, U.ulysses_a2a_4d, plan, 0, src, [dst[0], src[1] + 16], 0)     # dst on a src
     expect(-5, U.ulysses_a2a_4d, plan, 0, src, [dst[0], dst[0] + 16], 0)     # dst on a dst
+    msg = expect(-1, U.ulysses_a2a_4d, plan, 0, src, [dst[0], (1 << 64) - 16], 0)
+    assert "past the end of the address space" in msg
     # chunked: no cap, window too small for the cap, window overlapping
     expect(-1, U.ulysses_a2a_4d_chunked, plan, 0, src, dst, fake(2, off=1 << 37), 0)
     small = U.ulysses_plan_create(2, 1, 8, [3, 4], [1, 2], "bf16", 64)
