@@ -150,7 +150,6 @@ int plan_build(Plan *p, int world, int64_t b, int64_t d, const int64_t *seq_spli
             a.dst_pitch = p->R[r];
             a.dst_row0 = p->seq_off[j];
             a.dst_col0 = 0;
-            a.seq_pos0 = p->seq_off[j];
 
             Piece &c = p->mode[1].piece[j * world + r];
             c.j = j;
@@ -163,7 +162,6 @@ int plan_build(Plan *p, int world, int64_t b, int64_t d, const int64_t *seq_spli
             c.dst_pitch = p->G;
             c.dst_row0 = 0;
             c.dst_col0 = p->head_off[j] * hb;
-            c.seq_pos0 = p->seq_off[r];
         }
     for (int m = 0; m < 2; ++m)
         for (int q = 0; q < world * world; ++q) {

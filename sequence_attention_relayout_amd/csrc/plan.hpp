@@ -43,7 +43,6 @@ struct Piece {
     int64_t src_pitch = 0, dst_pitch = 0;
     int64_t src_row0 = 0, src_col0 = 0;
     int64_t dst_row0 = 0, dst_col0 = 0;
-    int64_t seq_pos0 = 0;    // global sequence position of the region's first row
 };
 
 struct ModeGeom {
