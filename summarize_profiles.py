@@ -75,12 +75,11 @@ WORKLOADS = [
     ("chunked_w4_qkv_plane_relayout", "relayout_kernel<false>", 224000000, 7168000000,
      "the plane-at-a-time W=4 QKV pack (250,000 tokens, 56 heads, d=128, bf16, 3 planes): the "
      "relayout of one plane, into the windows (staged) or straight into the destination plane "
-     "(direct)"),
+     "(direct); the whole-pack call launches the same kernel once per plane (each plane moves "
+     "7.2 GB)"),
     ("chunked_w4_qkv_plane_copy", "plane_copy_kernel", 224000000, 7168000000,
      "the same pack's copy of one plane from the W windows into the destination shards "
      "(staged mode only)"),
-    ("chunked_w4_qkv_one_pass", "relayout_kernel<true>", 672000000, 3 * 7168000000,
-     "the same pack's three planes in one relayout launch"),
 ]
 
 
@@ -97,17 +96,20 @@ def relayout_threads(world, b, d, S, H, esz, mode):
 
 def uneven_workloads():
     """The W=7 uneven relayout rows: one entry per byte width and mode (the
-    fp8 and int8 rows share a geometry, so they are summarised together)."""
+    fp8 and int8 rows share a geometry, so they are summarised together).
+    Each of their two batch planes moves 0.77-3.1 GB, so every plane gets a
+    launch of its own: one-plane grids and bytes per launch."""
     from sequence_attention_relayout_amd import workloads as W
     wl = W.workloads()["w7_uneven"]
     out = []
     for esz, name in ((2, "bf16"), (4, "fp32"), (1, "fp8_int8")):
         for mode in (0, 1):
             out.append((
-                f"w7_uneven_{name}_mode{mode}", "relayout_kernel<true>",
-                relayout_threads(wl.world, wl.b, wl.d, wl.seq_splits, wl.head_splits, esz, mode),
-                2 * wl.b * sum(wl.seq_splits) * sum(wl.head_splits) * wl.d * esz,
-                f"the uneven W=7 relayout, mode {mode}: b=2, s_global=75,597 as "
+                f"w7_uneven_{name}_mode{mode}", "relayout_kernel<false>",
+                relayout_threads(wl.world, 1, wl.d, wl.seq_splits, wl.head_splits, esz, mode),
+                2 * sum(wl.seq_splits) * sum(wl.head_splits) * wl.d * esz,
+                f"the uneven W=7 relayout, mode {mode}, one batch plane per launch (b=2): "
+                f"s_global=75,597 as "
                 f"{', '.join(f'{x:,}' for x in wl.seq_splits)}, heads "
                 f"{', '.join(map(str, wl.head_splits))}, d=128, "
                 + ("bf16" if esz == 2 else "fp32" if esz == 4 else
