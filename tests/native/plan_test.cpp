@@ -383,7 +383,7 @@ int main() {
     check_geometry(2, 1, 2048, 2, {3, 2}, {40, 24});
     check_geometry(3, 2, 8, 0, {50, 1, 77}, {1, 1, 1});
     check_geometry(4, 1, 16, 5, {9, 0, 33, 5}, {1, 1, 1, 1});
-    // the fused scatter at every head dimension it takes, with zero splits
+    // the fused pass at every head dimension it takes, with zero splits
     for (int it = 0; it < 60; ++it) {
         const int world = 1 + static_cast<int>(rng() % 8);
         const int64_t d = int64_t{8} << (it % 7);   // 8 .. 512
