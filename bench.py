@@ -503,10 +503,25 @@ def rows_qkv(U, W, torch, dev, stream, reps):
             U.ulysses_a2a_4d(plan, 0, xs[t], ys[t], h)
 
     med_three, _ = timed(three, reps, stream, torch)
+
+    def host_us(fn, n=20):
+        # host time to enqueue one q/k/v relayout while the GPU is busy with
+        # the previous ones (the calls return before their kernels run)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        t = (time.perf_counter() - t0) / n * 1e6
+        torch.cuda.synchronize()
+        return round(t, 2)
+
     rows["w8_qkv_mode0_one_launch"] = {"gbs": round(nb / (med_multi * 1e-3) / 1e9, 1),
-                                       "median_us": round(med_multi * 1e3, 1), "bytes": nb}
+                                       "median_us": round(med_multi * 1e3, 1), "bytes": nb,
+                                       "host_us_per_qkv": host_us(
+                                           lambda: U.ulysses_a2a_4d_multi(plan, 0, xs, ys, h))}
     rows["w8_qkv_mode0_three_launches"] = {"gbs": round(nb / (med_three * 1e-3) / 1e9, 1),
-                                           "median_us": round(med_three * 1e3, 1)}
+                                           "median_us": round(med_three * 1e3, 1),
+                                           "host_us_per_qkv": host_us(three)}
     # autograd: forward (mode 0) and backward (mode 1, same plan) of one tensor
     from sequence_attention_relayout_amd.autograd import all_to_all_4d
     xg = [x.detach().requires_grad_() for x in xs[0]]
