@@ -27,8 +27,9 @@
  * Ownership: the caller allocates and owns every device buffer (sources,
  * destinations, windows, gammas, rotary tables) and keeps it alive until the
  * stream work completes.  The library never allocates or frees device memory
- * and never synchronises a stream: each call validates on the host and then
- * enqueues asynchronously on the given stream.  A plan is host memory only,
+ * (the windows of ulysses_a2a_4d_chunked_static are a static array in the
+ * library's own code object) and never synchronises a stream: each call
+ * validates on the host and then enqueues asynchronously on the given stream.  A plan is host memory only,
  * immutable after creation, and may be shared by threads and reused.
  *
  * Errors: every call returns a status (ULYSSES_OK or a negative code below).
