@@ -244,6 +244,13 @@ def main():
           for r in range(wl.world)]
     torch.cuda.synchronize()
     h = stream.cuda_stream
+    # what the step reads: a checksum of both inputs' 32-bit words, summed on
+    # the device before anything is timed
+    checksum = int(sum(int(x.view(torch.int32).sum(dtype=torch.int64)) for x in x0 + y1))
+    inputs = {"generator": "torch.Generator on the device, one per shard set",
+              "seeds": {"mode0_input": wl.seed, "mode1_input": wl.seed + 1},
+              "values": "N(0,1) in fp32, rounded to bf16 by torch",
+              "checksum_int32_words": checksum}
 
     def mode0():
         U.ulysses_a2a_4d(plan, 0, x0, y0, h)
@@ -349,7 +356,8 @@ def main():
         "config": {"workload": "w8_wan720p: mode 0 + mode 1, W=8 emulated ranks, b=1, "
                                "s_global=75,600 (9,450/rank), n_global=40 (5/rank), d=128",
                    "world": 8, "b": 1, "s_global": 75600, "n_global": 40, "d": 128,
-                   "bytes_per_step": step_bytes, "parallelism": "none (one GPU)"},
+                   "bytes_per_step": step_bytes, "parallelism": "none (one GPU)",
+                   "inputs": inputs},
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "value_mall_cold": round(step_bytes / ((statistics.median(c0) + statistics.median(c1))
                                                * 1e-3) / 1e9, 1),
