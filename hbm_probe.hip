@@ -1,7 +1,9 @@
 // HBM ceilings of this GPU for the relayout's access pattern: pure read,
 // pure write and contiguous copy kernels moving 16-byte vectors with
 // non-temporal hints, in three launch shapes (64 x 1, 128 x 1 and 128 x 2
-// threads x vectors per thread), each moving 1,548,288,000 bytes (one
+// threads x vectors per thread) and, for the kernels that store, two store
+// policies (non-temporal, and non-temporal at device scope as the library
+// stores), each moving 1,548,288,000 bytes (one
 // relayout launch of the W=8, 75,600-token bf16 workload).  Measurement
 // infrastructure for the benchmark: it prints one JSON line per kernel and
 // shape (median of 20 timed runs after 3 warm-ups) and is not part of the
@@ -24,8 +26,22 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         }                                                                           \
     } while (0)
 
+// Store policy SC1: 0 non-temporal; 1 non-temporal at device scope (written
+// through the XCD's L2 at once).
+template <int SC1>
+__device__ __forceinline__ void store(u32x4 *p, u32x4 v) {
+    if constexpr (SC1)
+        // s_nop 0: the wait state a VALU write to the store's data registers
+        // needs after a store of more than 8 bytes (the compiler does not see
+        // this store to insert it)
+        asm volatile("global_store_dwordx4 %0, %1, off sc1 nt\n\ts_nop 0" ::"v"(p), "v"(v)
+                     : "memory");
+    else
+        __builtin_nontemporal_store(v, p);
+}
+
 // Block b moves vectors [B*U*b, B*U*(b+1)); lane t takes t, t + B, ...
-template <int B, int U>
+template <int B, int U, int SC1>
 __global__ void __launch_bounds__(B) copy_kernel(const u32x4 *__restrict__ s,
                                                  u32x4 *__restrict__ d, size_t n) {
     const size_t i = size_t(blockIdx.x) * (B * U) + threadIdx.x;
@@ -35,7 +51,7 @@ __global__ void __launch_bounds__(B) copy_kernel(const u32x4 *__restrict__ s,
         if (i + k * B < n) v[k] = __builtin_nontemporal_load(s + i + k * B);
 #pragma unroll
     for (int k = 0; k < U; ++k)
-        if (i + k * B < n) __builtin_nontemporal_store(v[k], d + i + k * B);
+        if (i + k * B < n) store<SC1>(d + i + k * B, v[k]);
 }
 
 template <int B, int U>
@@ -50,13 +66,13 @@ __global__ void __launch_bounds__(B) read_kernel(const u32x4 *__restrict__ s,
     if ((c.x & c.y & c.z & c.w) == 0xDEADBEEFu) sink[threadIdx.x] = c;
 }
 
-template <int B, int U>
+template <int B, int U, int SC1>
 __global__ void __launch_bounds__(B) write_kernel(u32x4 *__restrict__ d, size_t n) {
     const size_t i = size_t(blockIdx.x) * (B * U) + threadIdx.x;
     const u32x4 v = {static_cast<unsigned>(i), 1u, 2u, 3u};
 #pragma unroll
     for (int k = 0; k < U; ++k)
-        if (i + k * B < n) __builtin_nontemporal_store(v, d + i + k * B);
+        if (i + k * B < n) store<SC1>(d + i + k * B, v);
 }
 
 int main() {
@@ -85,7 +101,7 @@ int main() {
     hipEvent_t e0, e1;
     CHECK(hipEventCreate(&e0));
     CHECK(hipEventCreate(&e1));
-    auto run = [&](const char *kind, int blk, int u, auto launch) -> int {
+    auto run = [&](const char *kind, int blk, int u, const char *st, auto launch) -> int {
         std::vector<float> t;
         for (int r = 0; r < 23; ++r) {
             CHECK(hipEventRecord(e0, 0));
@@ -99,35 +115,39 @@ int main() {
         }
         std::sort(t.begin(), t.end());
         const float med = t[t.size() / 2];
-        std::printf("{\"kernel\": \"%s\", \"block\": %d, \"per_thread\": %d, \"bytes\": %zu, "
-                    "\"median_us\": %.1f, \"gbs\": %.1f}\n",
-                    kind, blk, u, moved, med * 1e3, moved / (med * 1e-3) / 1e9);
+        std::printf("{\"kernel\": \"%s\", \"block\": %d, \"per_thread\": %d, \"store\": \"%s\", "
+                    "\"bytes\": %zu, \"median_us\": %.1f, \"gbs\": %.1f}\n",
+                    kind, blk, u, st, moved, med * 1e3, moved / (med * 1e-3) / 1e9);
         std::fflush(stdout);
         return 0;
     };
     const u32x4 *src = reinterpret_cast<const u32x4 *>(a);
     u32x4 *dst = reinterpret_cast<u32x4 *>(b);
-#define SHAPE(B, U)                                                                        \
-    if (run("copy", B, U, [&] {                                                            \
-            copy_kernel<B, U><<<dim3(unsigned((n_copy + B * U - 1) / (B * U))), B>>>(      \
+#define STORES(B, U, SC1, ST)                                                              \
+    if (run("copy", B, U, ST, [&] {                                                        \
+            copy_kernel<B, U, SC1><<<dim3(unsigned((n_copy + B * U - 1) / (B * U))), B>>>( \
                 src, dst, n_copy);                                                         \
         }))                                                                                \
         return 1;                                                                          \
-    if (run("read", B, U, [&] {                                                            \
+    if (run("write", B, U, ST, [&] {                                                       \
+            write_kernel<B, U, SC1><<<dim3(unsigned((n_all + B * U - 1) / (B * U))), B>>>( \
+                dst, n_all);                                                               \
+        }))                                                                                \
+        return 1;
+#define SHAPE(B, U)                                                                        \
+    STORES(B, U, 0, "nt")                                                                  \
+    STORES(B, U, 1, "sc1 nt")                                                              \
+    if (run("read", B, U, "-", [&] {                                                       \
             read_kernel<B, U><<<dim3(unsigned((n_all + B * U - 1) / (B * U))), B>>>(src,   \
                                                                                  sink,     \
                                                                                  n_all);   \
-        }))                                                                                \
-        return 1;                                                                          \
-    if (run("write", B, U, [&] {                                                           \
-            write_kernel<B, U><<<dim3(unsigned((n_all + B * U - 1) / (B * U))), B>>>(dst,  \
-                                                                                  n_all);  \
         }))                                                                                \
         return 1;
     SHAPE(64, 1)
     SHAPE(128, 1)
     SHAPE(128, 2)
 #undef SHAPE
+#undef STORES
     CHECK(hipDeviceSynchronize());
     CHECK(hipFree(a));
     CHECK(hipFree(b));
