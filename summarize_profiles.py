@@ -61,23 +61,28 @@ CUS, SIMDS, XCDS = 256, 1024, 8
 CALIBRATION = ("__amd_rocclr_copyBuffer", 131072)
 CALIBRATION_BYTES = 774144000   # each way: bench.py's same-run device-to-device copy
 
-# (file stem, kernel, total grid threads, algorithmic bytes per launch, what)
+# Mode-0 and mode-1 launches of the one-plane relayout (mode 0 runs its
+# blocks in the two-halves order).
+MODE0, MODE1 = "relayout_kernel<false, true>", "relayout_kernel<false, false>"
+
+# (file stem, kernels whose dispatches are pooled, total grid threads,
+# algorithmic bytes per launch, what)
 WORKLOADS = [
-    ("relayout_w8_wan720p", "relayout_kernel<false>", 48384000, 1548288000,
+    ("relayout_w8_wan720p", (MODE0, MODE1), 48384000, 1548288000,
      "the relayout at W=8, 75,600 tokens (9,450 per rank), 40 heads (5 per rank), d=128, bf16: "
      "the step's mode-0 and mode-1 launches and the rows' launches of the same geometry "
      "(q/k/v one at a time, the autograd forward and backward, the fused row's plain v)"),
-    ("fused_qknorm_rope_w8_wan720p", "fused_kernel<16, false>", 48384000,
+    ("fused_qknorm_rope_w8_wan720p", ("fused_kernel<16, false>",), 48384000,
      2 * 1548288000 + 2 * 75600 * 64 * 4 + 2 * 128 * 4,
      "the fused QK RMSNorm + RoPE mode-0 pass at the same W=8 geometry, q and k in one launch "
      "(algorithmic bytes: q and k each read and written once, the two 75,600 x 64 fp32 rotary "
      "tables and the two 128-float gains read once)"),
-    ("chunked_w4_qkv_plane_relayout", "relayout_kernel<false>", 224000000, 7168000000,
+    ("chunked_w4_qkv_plane_relayout", (MODE0,), 224000000, 7168000000,
      "the plane-at-a-time W=4 QKV pack (250,000 tokens, 56 heads, d=128, bf16, 3 planes): the "
      "relayout of one plane, into the windows (staged) or straight into the destination plane "
      "(direct); the whole-pack call launches the same kernel once per plane (each plane moves "
      "7.2 GB)"),
-    ("chunked_w4_qkv_plane_copy", "plane_copy_kernel", 224000000, 7168000000,
+    ("chunked_w4_qkv_plane_copy", ("plane_copy_kernel",), 224000000, 7168000000,
      "the same pack's copy of one plane from the W windows into the destination shards "
      "(staged mode only)"),
 ]
@@ -105,7 +110,7 @@ def uneven_workloads():
     for esz, name in ((2, "bf16"), (4, "fp32"), (1, "fp8_int8")):
         for mode in (0, 1):
             out.append((
-                f"w7_uneven_{name}_mode{mode}", "relayout_kernel<false>",
+                f"w7_uneven_{name}_mode{mode}", (MODE1 if mode else MODE0,),
                 relayout_threads(wl.world, 1, wl.d, wl.seq_splits, wl.head_splits, esz, mode),
                 2 * sum(wl.seq_splits) * sum(wl.head_splits) * wl.d * esz,
                 f"the uneven W=7 relayout, mode {mode}, one batch plane per launch (b=2): "
@@ -155,6 +160,19 @@ def bench_line(out):
     return json.loads(lines[-1]) if lines else None
 
 
+def pooled(tr, cm, cn, kerns, grid):
+    """Trace durations, mean counters and dispatch counts of every kernel in
+    kerns at this grid size, pooled over their dispatches."""
+    ds = [x for k in kerns for x in tr.get((k, grid), [])]
+    tot, cnt = defaultdict(float), defaultdict(int)
+    for k in kerns:
+        for c, v in cm.get((k, grid), {}).items():
+            n = cn[(k, grid)][c]
+            tot[c] += v * n
+            cnt[c] += n
+    return ds, {c: tot[c] / cnt[c] for c in tot}, dict(cnt)
+
+
 def stats_row(name, ds):
     return (f"| `{name}` | {len(ds)} | {statistics.mean(ds):.1f} | {statistics.median(ds):.1f} "
             f"| {min(ds):.1f} | {max(ds):.1f} |")
@@ -186,9 +204,9 @@ def main():
     write_factor = CALIBRATION_BYTES / (cal["WRITE_SIZE"] * 1024) if "WRITE_SIZE" in cal else None
     cal_trace = tr.get(CALIBRATION, [])
     table = []
-    for stem, kern, grid, nbytes, what in WORKLOADS + uneven_workloads():
-        ds = tr.get((kern, grid), [])
-        c = cm.get((kern, grid), {})
+    for stem, kerns, grid, nbytes, what in WORKLOADS + uneven_workloads():
+        ds, c, counts = pooled(tr, cm, cn, kerns, grid)
+        kern = " + ".join(kerns)
         if not ds:
             print(f"{stem}: no dispatches of {kern} with {grid} threads in the trace",
                   file=sys.stderr)
@@ -201,9 +219,13 @@ def main():
             "Command (from /tmp with TMPDIR=/tmp, on one MI355X; REPO is this repository, OUT "
             "any output folder), then `python3 REPO/summarize_profiles.py OUT`:", "",
             "```", TRACE_CMD, "```", "",
-            f"Dispatches summarised: every `{kern}` launch of {grid:,} threads.", "",
+            f"Dispatches summarised: every {' and every '.join(f'`{k}`' for k in kerns)} launch "
+            f"of {grid:,} threads.", "",
             "| Kernel | Dispatches | Average (us) | Median (us) | Min (us) | Max (us) |",
-            "|---|---|---|---|---|---|", stats_row(kern, ds)]
+            "|---|---|---|---|---|---|"]
+        lines += [stats_row(k, tr[(k, grid)]) for k in kerns if tr.get((k, grid))]
+        if len(kerns) > 1:
+            lines.append(stats_row("all of the above", ds).replace("`", ""))
         if cal_trace:
             lines.append(stats_row("__amd_rocclr_copyBuffer", cal_trace)
                          + "  (torch device-to-device copy of 774,144,000 B, same run)")
@@ -229,8 +251,7 @@ def main():
                          f" (calibrated traffic / algorithmic bytes = {traffic / nbytes:.5f}).")
             j = {
                 "kernel": kern, "grid_threads": grid, "what": what,
-                "dispatches_counted": [cn[(kern, grid)]["FETCH_SIZE"],
-                                       cn[(kern, grid)]["WRITE_SIZE"]],
+                "dispatches_counted": [counts["FETCH_SIZE"], counts["WRITE_SIZE"]],
                 "commands": [pmc_cmd("fetch"), pmc_cmd("write"), pmc_cmd("rdreq"),
                              pmc_cmd("wrreq")],
                 "fetch_kib_per_dispatch": round(c["FETCH_SIZE"], 2),
