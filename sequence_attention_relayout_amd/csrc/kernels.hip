@@ -175,9 +175,10 @@ hipError_t launch_relayout(const RelayoutArgs &a, uint32_t grid_x, uint32_t plan
                            stream);
 }
 
-// One batch plane per rank, window -> destination plane, contiguous.
+// One batch plane per rank, window -> destination plane, contiguous, in
+// halves() order (a plain copy is the case that order was measured on).
 __global__ void __launch_bounds__(kRelayoutBlock) plane_copy_kernel(const CopyArgs a) {
-    const uint32_t x = blockIdx.x;
+    const uint32_t x = halves(blockIdx.x, gridDim.x);
     const uint32_t r = find_group(a.blk_begin, x);
     const uint32_t v = (x - a.blk_begin[r]) * kRelayoutBlock + threadIdx.x;
     if (v < a.nvec[r])
