@@ -239,8 +239,10 @@ hipError_t launch_plane_copy(const CopyArgs &a, uint32_t grid_x, hipStream_t str
 // reads both from the source rank that owns the row's sequence position, and
 // stores them normalised and rotated, so every store of a wave is one
 // contiguous KiB.  Measured on MI355X it beats walking the sources (a
-// scatter) by 3-6%; the data movement alone, with the arithmetic and the
-// tables taken out, runs at the same speed, so the arithmetic is hidden.
+// scatter) by 3-6%.  With the arithmetic and the tables taken out, the data
+// movement alone runs only 2-6% faster: moving two tensors per lane is what
+// bounds the pass, and layouts with one tensor per lane or per block, or
+// with more concurrent streams, measured slower.
 //
 // A head row of d bf16 elements is L = d/8 16-byte vectors held by L
 // consecutive lanes: lane l of the row holds elements 8l .. 8l+7 and rotary
