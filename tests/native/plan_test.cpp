@@ -53,6 +53,15 @@ static uint32_t find_group(const uint32_t *begin, uint32_t x) {
     return g;
 }
 
+// The kernels' two-halves block order: of a launch's n blocks, block x
+// takes block x / 2 (x even) or ceil(n / 2) + x / 2 (x odd).  Mode 0 of the
+// relayout, the plane copy and the fused pass run their blocks in this
+// order; replaying them through it checks, for every geometry here, that
+// each vector is still written exactly once.
+static uint32_t halves(uint32_t x, uint32_t n) {
+    return (x & 1) ? ((n + 1) >> 1) + (x >> 1) : (x >> 1);
+}
+
 // The kernels' split_rows, with the bound on the multiply-high numerator.
 static void split_rows(const RowSplit &rs, uint32_t s0, uint32_t lane, uint32_t *row,
                        uint32_t *col) {
@@ -107,8 +116,9 @@ static void check_relayout(const Plan &p, int mode, uint32_t per_launch, uint32_
         const uint32_t planes = static_cast<uint32_t>(std::min<int64_t>(per_launch, p.b - p0));
         for (uint32_t t = 0; t < tensors; ++t)
             for (uint32_t y = 0; y < planes; ++y)
-                for (uint32_t x = 0; x < gx; ++x)
+                for (uint32_t xb = 0; xb < gx; ++xb)
                     for (uint32_t lane = 0; lane < kRelayoutBlock; ++lane) {
+                        const uint32_t x = mode == 0 ? halves(xb, uint32_t(gx)) : xb;
                         const uint32_t r = find_group(a.blk_begin, x);
                         REQUIRE(r < uint32_t(p.world), "block past the world");
                         const uint32_t s0 = (x - a.blk_begin[r]) * kRelayoutBlock;
@@ -154,8 +164,9 @@ static void check_plane_copy(const Plan &p, int mode) {
     std::vector<std::vector<int>> hits(p.world);
     for (int r = 0; r < p.world; ++r)
         hits[r].assign(static_cast<size_t>(p.mode[mode].dst_plane[r] / 16), 0);
-    for (uint32_t x = 0; x < gc; ++x)
+    for (uint32_t xb = 0; xb < gc; ++xb)
         for (uint32_t lane = 0; lane < kRelayoutBlock; ++lane) {
+            const uint32_t x = halves(xb, uint32_t(gc));
             const uint32_t r = find_group(c.blk_begin, x);
             REQUIRE(r < uint32_t(p.world), "copy block past the world");
             const uint32_t v = (x - c.blk_begin[r]) * kRelayoutBlock + lane;
@@ -181,7 +192,8 @@ static void check_fused(const Plan &p) {
     std::vector<std::vector<int>> hits(p.world);
     for (int r = 0; r < p.world; ++r) hits[r].assign(static_cast<size_t>(p.b * g.dst_plane[r] / 16), 0);
     for (uint32_t y = 0; y < p.b; ++y)
-        for (uint32_t x = 0; x < gx; ++x) {
+        for (uint32_t xb = 0; xb < gx; ++xb) {
+            const uint32_t x = halves(xb, uint32_t(gx));
             const uint32_t r = find_group(a.blk_begin, x);
             REQUIRE(r < uint32_t(p.world), "fused block past the world");
             const uint32_t s0 = (x - a.blk_begin[r]) * kFusedBlock;
